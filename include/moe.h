@@ -1,0 +1,230 @@
+/*
+ * moe.h -- C ABI of libmoe, a routed mixture-of-experts forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation ("Experts backends" page, opening paragraph): for every token
+ * a router selects k of E experts; the token's hidden state is projected
+ * through each selected expert's parameters and the k results are summed with
+ * the routing weights.  Each expert is a gated MLP (backend table, row
+ * deepgemm_megamoe; section "SonicMoE"): an up projection with a silu-gated
+ * twin (SwiGLU), then a down projection.  Tokens are first ordered by their
+ * selected expert so that all experts run as one grouped GEMM (backend table,
+ * rows grouped_mm and deepgemm).
+ *
+ * Notation: T tokens, H hidden size, I expert intermediate size, E experts,
+ * k experts per token, P = T*k (token, slot) pairs.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     marked "host".  The library never allocates or frees device memory; it
+ *     uses only the caller's buffers and the caller's workspace `ws`, sized by
+ *     moe_workspace_bytes().  Buffers must stay alive until the stream has
+ *     finished the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     only enqueue work on it: they never synchronise and never read device
+ *     memory back to the host, so a whole forward can be captured in a graph.
+ *   - All tensors are dense and row-major.  x and out are [T,H]; w_router is
+ *     [E,H]; w_gate and w_up are [E,I,H]; w_down is [E,H,I] (each matrix is
+ *     [out_features, in_features]).
+ *   - Validation happens on the host before anything is launched.  A bad
+ *     argument returns MOE_EINVAL, an unsupported combination MOE_EUNSUPPORTED,
+ *     a too-small workspace MOE_EWORKSPACE, a failed launch MOE_EHIP; in every
+ *     error case nothing has been enqueued.  No C++ exception crosses the ABI.
+ *     moe_last_error() describes the last failure of the calling thread.
+ *   - T = 0 is valid: the calls write the empty results (zero counts and
+ *     offsets) and return MOE_OK.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,          /* bad pointer, shape or enum value */
+    MOE_EUNSUPPORTED = 2,    /* valid request this library does not implement */
+    MOE_EWORKSPACE = 3,      /* ws is NULL or smaller than moe_workspace_bytes() */
+    MOE_EHIP = 4             /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2 } moe_dtype;
+
+/* Router score, applied to key[e] = x . w_router[e] + router_bias[e].
+ * Experts are selected by descending key, ties to the lowest expert index. */
+typedef enum {
+    MOE_SCORE_SOFTMAX = 0,   /* softmax over all E keys */
+    MOE_SCORE_SIGMOID = 1    /* 1 / (1 + exp(-key)) */
+} moe_score;
+
+/* FP8 weight block scales (the paragraph under the backend table: float32 or
+ * UE8M0 scales).  F32: one float per block.  UE8M0: one byte b per block with
+ * value 2^(b-127) (0xff is NaN). */
+typedef enum { MOE_SCALE_NONE = 0, MOE_SCALE_F32 = 1, MOE_SCALE_UE8M0 = 2 } moe_scale_fmt;
+
+/* FP8 activation scheme (section "FP8 and FP4 quantized experts": dynamic
+ * per-row scales are required, static per-tensor scales are rejected). */
+typedef enum { MOE_ACT_NONE = 0, MOE_ACT_DYNAMIC = 1, MOE_ACT_STATIC = 2 } moe_act_scheme;
+
+/* Expert-GEMM strategy of moe_forward.  GROUPED runs tiled grouped GEMMs over
+ * the expert-sorted rows; STREAM reads every touched expert's weights exactly
+ * once, split over all compute units (for decode-sized batches, T <= 64; the
+ * section "Decode-stage switching" notes that small token counts want a
+ * different scheme); AUTO picks STREAM when T <= 64. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } moe_path;
+
+typedef enum {
+    MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GATE_UP = 2, MOE_OP_DOWN = 3,
+    MOE_OP_COMBINE = 4, MOE_OP_FORWARD = 5
+} moe_op;
+
+/* Layer description (host memory, read during the call only). */
+typedef struct moe_desc {
+    int64_t T;             /* tokens, >= 0 */
+    int32_t H;             /* hidden size, multiple of 16 (of 128 for fp8) */
+    int32_t I;             /* expert intermediate size, multiple of 16 (of 128 for fp8) */
+    int32_t E;             /* experts, 1..256 */
+    int32_t k;             /* experts per token, 1..min(E, 32) */
+    int32_t score;         /* moe_score */
+    int32_t renormalize;   /* 1: selected scores are divided by their sum */
+    float routed_scale;    /* multiplies the final routing weights */
+    int32_t act_dtype;     /* MOE_DT_F32 or MOE_DT_BF16: x, w_router and out */
+    int32_t w_dtype;       /* expert weights: MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3 */
+    int32_t w_scale_fmt;   /* MOE_SCALE_NONE, or F32 / UE8M0 with FP8 weights */
+    int32_t block;         /* FP8 weight block edge and activation group: 128 (else 0) */
+    int32_t act_scheme;    /* MOE_ACT_NONE, or MOE_ACT_DYNAMIC with FP8 weights */
+    int32_t y_dtype;       /* expert-output rows y_sorted: MOE_DT_F32 or MOE_DT_BF16 */
+    int32_t path;          /* moe_path */
+    int32_t reserved[3];   /* must be zero */
+} moe_desc;
+
+/* Supported combinations:
+ *   act F32  + weights F32            (fp32 everywhere; h is fp32)
+ *   act BF16 + weights BF16           (bf16 MFMA, fp32 accumulate; h is bf16)
+ *   act BF16 + weights FP8_E4M3, scales F32 or UE8M0, block 128, act DYNAMIC
+ *            (x and h are quantized to e4m3 per row per 128 channels with
+ *             fp32 scales amax/448; fp8 MFMA, fp32 accumulate, block scales
+ *             applied per 128-deep K chunk in fp32)
+ * Intermediate h [P,I] is in the expert weight format (bf16/f32, or e4m3 codes
+ * plus fp32 scales [P,I/128]). */
+
+/* ------------------------------------------------------------------------ */
+
+/* Router (opening paragraph: "a router selects k experts").
+ *   x           [T,H] act_dtype
+ *   w_router    [E,H] act_dtype
+ *   router_bias [E] fp32, added to the logits before scoring, or NULL
+ *   topk_ids    [T,k] int32 out: selected experts, descending key, ties to
+ *               the lowest index
+ *   topk_w      [T,k] fp32 out: score of each selected expert (softmax over
+ *               all E, or sigmoid), divided by the sum of the k selected scores
+ *               if desc->renormalize, times desc->routed_scale
+ * Logits accumulate in fp32. */
+moe_status moe_route_topk(const moe_desc* desc, const void* x, const void* w_router,
+                          const float* router_bias, int32_t* topk_ids, float* topk_w,
+                          void* stream);
+
+/* Order (token, slot) pairs by expert (backend table, rows grouped_mm and
+ * deepgemm: tokens are ordered / sorted by selected expert).
+ *   topk_ids        [T,k] int32 in, values in [0,E) (a pair with an id outside
+ *                   that range is left out of counts; its perm/inv entries are
+ *                   then undefined)
+ *   counts          [E] out: pairs per expert
+ *   offsets         [E+1] out: exclusive prefix sum of counts
+ *   perm            [P] out: perm[row] = t*k + i, rows of one expert in
+ *                   ascending (t, i) order (stable)
+ *   inv             [P] out: inv[t*k + i] = row
+ *   x, x_sorted     optional gather ([T,H] in, [P,H] out), both NULL or both
+ *                   set.  With FP8 weights x_sorted receives e4m3 codes and
+ *                   x_sorted_scales [P,H/128] fp32 the dynamic per-row scales;
+ *                   otherwise x_sorted has act_dtype and x_sorted_scales is NULL.
+ *   ws, ws_bytes    workspace of moe_workspace_bytes(desc, MOE_OP_PERMUTE) */
+moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, const void* x,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                       void* x_sorted, float* x_sorted_scales,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Gate/up grouped GEMM with the SwiGLU epilogue, all experts in one launch.
+ * Row r of expert e (offsets[e] <= r < offsets[e+1]):
+ *   h[r, j] = silu(g) * u,  g = x_sorted[r] . w_gate[e, j],  u = x_sorted[r] . w_up[e, j]
+ *   x_sorted      [P,H] act_dtype, or e4m3 codes with x_scales [P,H/128] (FP8)
+ *   offsets       [E+1] from moe_permute
+ *   w_gate, w_up  [E,I,H]; with FP8 also w_gate_scales, w_up_scales
+ *                 [E,I/128,H/128] (fp32 or UE8M0 bytes), else NULL
+ *   h             [P,I] out: weight format (f32 / bf16), or e4m3 codes with
+ *                 h_scales [P,I/128] fp32 (FP8: dynamic per-row quantization)
+ *   ws, ws_bytes  workspace of moe_workspace_bytes(desc, MOE_OP_GATE_UP) */
+moe_status moe_expert_gate_up_swiglu(const moe_desc* desc, const void* x_sorted,
+                                     const float* x_scales, const int32_t* offsets,
+                                     const void* w_gate, const void* w_up,
+                                     const void* w_gate_scales, const void* w_up_scales,
+                                     void* h, float* h_scales,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* Down-projection grouped GEMM: y_sorted[r, o] = h[r] . w_down[e, o].
+ *   h, h_scales   as written by moe_expert_gate_up_swiglu
+ *   w_down        [E,H,I]; with FP8 w_down_scales [E,H/128,I/128], else NULL
+ *   y_sorted      [P,H] out, desc->y_dtype
+ *   ws, ws_bytes  workspace of moe_workspace_bytes(desc, MOE_OP_DOWN) */
+moe_status moe_expert_down(const moe_desc* desc, const void* h, const float* h_scales,
+                           const int32_t* offsets, const void* w_down,
+                           const void* w_down_scales, void* y_sorted,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine back to token order (opening paragraph: "aggregated with
+ * routing weights"):
+ *   out[t, :] = sum_{i<k} topk_w[t, i] * y_sorted[inv[t*k + i], :]
+ * summed in fp32 in slot order, rounded once to act_dtype.  No atomics: the
+ * result is bitwise reproducible. */
+moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_sorted,
+                                 const int32_t* inv, const float* topk_w, void* out,
+                                 void* stream);
+
+/* The whole layer in one call: route, permute, (FP8: quantize x), gate/up +
+ * SwiGLU, down, combine.  The gate/up GEMM reads x rows through the
+ * permutation, so no sorted copy of x is made.
+ *   topk_ids_out, topk_w_out  [T,k] optional copies of the routing (NULL: kept
+ *                             in the workspace)
+ *   counts_out                [E] optional pairs per expert
+ *   ws, ws_bytes              workspace of moe_workspace_bytes(desc, MOE_OP_FORWARD) */
+moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router,
+                       const float* router_bias, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* w_gate_scales,
+                       const void* w_up_scales, const void* w_down_scales, void* out,
+                       int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by `op` (a moe_op) for this description; 0 if the
+ * op needs none or the description is invalid (the call itself then reports
+ * why). */
+size_t moe_workspace_bytes(const moe_desc* desc, int op);
+
+/* Static text for a moe_status value. */
+const char* moe_status_str(int status);
+
+/* Text of the last failure in the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Stage timing, for measurement.  While enabled, moe_forward brackets each of
+ * its kernels with HIP events on the caller's stream.  moe_timing_read waits
+ * for the recorded events, adds their elapsed times into ms[stage] and the
+ * number of timed launches into launches[stage] (both host arrays of
+ * MOE_NUM_STAGES entries), and clears the record.  Not thread-safe. */
+enum {
+    MOE_STAGE_ROUTE = 0, MOE_STAGE_HIST = 1, MOE_STAGE_SCAN = 2, MOE_STAGE_SCATTER = 3,
+    MOE_STAGE_QUANT_X = 4, MOE_STAGE_GATE_UP = 5, MOE_STAGE_DOWN = 6, MOE_STAGE_COMBINE = 7,
+    MOE_NUM_STAGES = 8
+};
+moe_status moe_timing_enable(int on);
+moe_status moe_timing_read(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,563 @@
+// libmoe host side: argument validation, workspace layout, launch sequences
+// and stage timing.  The C ABI is declared in include/moe.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY_HIP(expr, what)                      \
+  do {                                               \
+    hipError_t e_ = (expr);                          \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int64_t pairs(const moe_desc* d) { return d->T * (int64_t)d->k; }
+
+size_t elt_bytes(int dt) { return dt == MOE_DT_F32 ? 4 : dt == MOE_DT_BF16 ? 2 : 1; }
+
+bool is_fp8(const moe_desc* d) { return d->w_dtype == MOE_DT_FP8_E4M3; }
+
+moe_status validate(const moe_desc* d) {
+  if (!d) return fail(MOE_EINVAL, "desc is NULL");
+  if (d->T < 0) return fail(MOE_EINVAL, "T = %lld < 0", (long long)d->T);
+  if (d->H <= 0 || d->I <= 0) return fail(MOE_EINVAL, "H = %d, I = %d must be positive", d->H, d->I);
+  if (d->E < 1 || d->E > kMaxExperts) return fail(MOE_EINVAL, "E = %d outside 1..%d", d->E, kMaxExperts);
+  if (d->k < 1 || d->k > d->E) return fail(MOE_EINVAL, "k = %d outside 1..E (E = %d)", d->k, d->E);
+  if (d->k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "k = %d above %d", d->k, kMaxTopK);
+  if (d->score != MOE_SCORE_SOFTMAX && d->score != MOE_SCORE_SIGMOID)
+    return fail(MOE_EINVAL, "score = %d", d->score);
+  if (d->renormalize != 0 && d->renormalize != 1)
+    return fail(MOE_EINVAL, "renormalize = %d", d->renormalize);
+  if (!std::isfinite(d->routed_scale)) return fail(MOE_EINVAL, "routed_scale is not finite");
+  if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16)
+    return fail(MOE_EINVAL, "act_dtype = %d", d->act_dtype);
+  if (d->w_dtype != MOE_DT_F32 && d->w_dtype != MOE_DT_BF16 && d->w_dtype != MOE_DT_FP8_E4M3)
+    return fail(MOE_EINVAL, "w_dtype = %d", d->w_dtype);
+  if (d->y_dtype != MOE_DT_F32 && d->y_dtype != MOE_DT_BF16)
+    return fail(MOE_EINVAL, "y_dtype = %d", d->y_dtype);
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_STREAM) return fail(MOE_EINVAL, "path = %d", d->path);
+  for (int r : d->reserved)
+    if (r != 0) return fail(MOE_EINVAL, "reserved fields must be zero");
+  if (d->T * (int64_t)d->k > (int64_t)INT32_MAX / 2)
+    return fail(MOE_EUNSUPPORTED, "T*k = %lld too large", (long long)(d->T * d->k));
+  if (d->w_scale_fmt < MOE_SCALE_NONE || d->w_scale_fmt > MOE_SCALE_UE8M0)
+    return fail(MOE_EINVAL, "w_scale_fmt = %d", d->w_scale_fmt);
+  if (d->act_scheme < MOE_ACT_NONE || d->act_scheme > MOE_ACT_STATIC)
+    return fail(MOE_EINVAL, "act_scheme = %d", d->act_scheme);
+
+  if (d->w_dtype == MOE_DT_FP8_E4M3) {
+    if (d->act_dtype != MOE_DT_BF16)
+      return fail(MOE_EUNSUPPORTED, "fp8 experts need bf16 activations");
+    if (d->w_scale_fmt == MOE_SCALE_NONE)
+      return fail(MOE_EINVAL, "fp8 experts need block scales (F32 or UE8M0)");
+    if (d->block != 128) return fail(MOE_EUNSUPPORTED, "fp8 block = %d; only 128 is supported", d->block);
+    if (d->act_scheme == MOE_ACT_STATIC)
+      return fail(MOE_EUNSUPPORTED,
+                  "static (per-tensor) activation quantization is rejected; use dynamic per-row scales");
+    if (d->act_scheme != MOE_ACT_DYNAMIC)
+      return fail(MOE_EINVAL, "fp8 experts need act_scheme = MOE_ACT_DYNAMIC");
+    if (d->H % 128 || d->I % 128)
+      return fail(MOE_EUNSUPPORTED, "fp8 experts need H and I multiples of 128 (H = %d, I = %d)", d->H, d->I);
+  } else {
+    if (d->w_scale_fmt != MOE_SCALE_NONE) return fail(MOE_EINVAL, "block scales given for unquantized experts");
+    if (d->act_scheme != MOE_ACT_NONE) return fail(MOE_EINVAL, "act_scheme set for unquantized experts");
+    if (d->act_dtype != d->w_dtype)
+      return fail(MOE_EUNSUPPORTED, "activation and expert dtypes differ (%d vs %d)", d->act_dtype, d->w_dtype);
+    if (d->w_dtype == MOE_DT_BF16 && (d->H % 64 || d->I % 64))
+      return fail(MOE_EUNSUPPORTED, "bf16 experts need H and I multiples of 64 (H = %d, I = %d)", d->H, d->I);
+    if (d->w_dtype == MOE_DT_F32 && (d->H % 8 || d->I % 8))
+      return fail(MOE_EUNSUPPORTED, "fp32 experts need H and I multiples of 8");
+  }
+  if (d->path == MOE_PATH_STREAM)
+    return fail(MOE_EUNSUPPORTED, "the weight-streaming path is not available in this build");
+  return MOE_OK;
+}
+
+// ---- workspace layout ----------------------------------------------------
+
+struct Carve {
+  uint8_t* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+int gate_up_ntiles(const moe_desc* d) { return (d->I + kGemmGateUpChannels - 1) / kGemmGateUpChannels; }
+int down_ntiles(const moe_desc* d) { return (d->H + kGemmDownChannels - 1) / kGemmDownChannels; }
+
+int64_t sched_capacity(const moe_desc* d, int ntiles) {
+  const int64_t P = pairs(d);
+  const int64_t tiles = (P + kGemmRowsPerTile - 1) / kGemmRowsPerTile + std::min<int64_t>(d->E, P);
+  return tiles * ntiles;
+}
+
+size_t sched_bytes(int64_t cap) { return sizeof(Schedule) + (size_t)cap * sizeof(WorkItem); }
+
+int grid_for(int64_t cap) { return (int)((cap + kNumXcd - 1) / kNumXcd * kNumXcd); }
+
+struct PermuteWs {
+  int32_t* block_counts;
+  int32_t* block_base;
+  uint8_t* xq;
+  float* xs;
+};
+
+PermuteWs carve_permute(Carve& c, const moe_desc* d, bool with_quant) {
+  const int64_t nb = perm_blocks(pairs(d));
+  PermuteWs w{};
+  w.block_counts = c.take<int32_t>((size_t)nb * d->E);
+  w.block_base = c.take<int32_t>((size_t)nb * d->E);
+  if (with_quant) {
+    w.xq = c.take<uint8_t>((size_t)d->T * d->H);
+    w.xs = c.take<float>((size_t)d->T * (d->H / 128));
+  }
+  return w;
+}
+
+struct ForwardWs {
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  PermuteWs pw;
+  int32_t* perm;
+  int32_t* inv;
+  int32_t* touched;
+  Schedule* sched_gu;
+  Schedule* sched_dn;
+  void* h;
+  float* hs;
+  void* y;
+};
+
+ForwardWs carve_forward(Carve& c, const moe_desc* d) {
+  const int64_t P = pairs(d);
+  ForwardWs w{};
+  w.ids = c.take<int32_t>(P);
+  w.w = c.take<float>(P);
+  w.counts = c.take<int32_t>(d->E);
+  w.offsets = c.take<int32_t>(d->E + 1);
+  w.pw = carve_permute(c, d, is_fp8(d));
+  w.perm = c.take<int32_t>(P);
+  w.inv = c.take<int32_t>(P);
+  w.touched = c.take<int32_t>(d->E + 1);
+  if (d->w_dtype != MOE_DT_F32) {
+    w.sched_gu = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
+    w.sched_dn = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, down_ntiles(d))));
+  }
+  w.h = c.take<uint8_t>((size_t)P * d->I * elt_bytes(d->w_dtype));
+  if (is_fp8(d)) w.hs = c.take<float>((size_t)P * (d->I / 128));
+  w.y = c.take<uint8_t>((size_t)P * d->H * elt_bytes(d->y_dtype));
+  return w;
+}
+
+size_t ws_size(const moe_desc* d, int op) {
+  Carve c{nullptr};
+  switch (op) {
+    case MOE_OP_ROUTE: return 0;
+    case MOE_OP_PERMUTE: carve_permute(c, d, is_fp8(d)); return c.off;
+    case MOE_OP_GATE_UP:
+      return d->w_dtype == MOE_DT_F32 ? 0 : align_up(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
+    case MOE_OP_DOWN:
+      return d->w_dtype == MOE_DT_F32 ? 0 : align_up(sched_bytes(sched_capacity(d, down_ntiles(d))));
+    case MOE_OP_COMBINE: return 0;
+    case MOE_OP_FORWARD: carve_forward(c, d); return c.off;
+    default: return 0;
+  }
+}
+
+moe_status check_ws(const moe_desc* d, int op, void* ws, size_t ws_bytes) {
+  size_t need = ws_size(d, op);
+  if (need == 0) return MOE_OK;
+  if (!ws || ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                ws ? "" : " (NULL)");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+// ---- stage timing ----------------------------------------------------------
+
+struct TimedLaunch {
+  int stage;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct StageTimer {
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageTimer(int st, hipStream_t stream) : stage(st), s(stream) {
+    if (!g_timing) return;
+    a = pool_event();
+    b = pool_event();
+    if (a && b) hipEventRecord(a, s);
+  }
+  ~StageTimer() {
+    if (!g_timing || !a || !b) return;
+    hipEventRecord(b, s);
+    g_pending.push_back({stage, a, b});
+  }
+};
+
+// ---- launch sequences --------------------------------------------------------
+
+SchedRequest sched_req(Schedule* s, const moe_desc* d, int ntiles) {
+  SchedRequest r{};
+  r.sched = s;
+  r.rows_per_tile = kGemmRowsPerTile;
+  r.ntiles = ntiles;
+  r.capacity = (int)sched_capacity(d, ntiles);
+  return r;
+}
+
+moe_status run_permute(const moe_desc* d, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* inv, int32_t* touched, const PermuteWs& pw,
+                       SchedRequest s0, SchedRequest s1, hipStream_t st) {
+  const int64_t P = pairs(d);
+  const int64_t nb = perm_blocks(P);
+  {
+    StageTimer tm(MOE_STAGE_HIST, st);
+    MOE_TRY_HIP(launch_hist(ids, P, d->E, pw.block_counts, st), "histogram launch");
+  }
+  {
+    StageTimer tm(MOE_STAGE_SCAN, st);
+    MOE_TRY_HIP(launch_scan(pw.block_counts, nb, d->E, counts, offsets, pw.block_base, touched, s0, s1, st),
+                "scan launch");
+  }
+  {
+    StageTimer tm(MOE_STAGE_SCATTER, st);
+    MOE_TRY_HIP(launch_scatter(ids, P, d->E, pw.block_base, perm, inv, st), "scatter launch");
+  }
+  return MOE_OK;
+}
+
+GemmArgs gemm_common(const moe_desc* d) {
+  GemmArgs a{};
+  a.E = d->E;
+  a.P = pairs(d);
+  a.scale_ue8m0 = d->w_scale_fmt == MOE_SCALE_UE8M0;
+  return a;
+}
+
+moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scales, const int32_t* gather,
+                       const int32_t* offsets, const void* wg, const void* wu, const void* sg,
+                       const void* su, void* h, float* hs, const Schedule* sched, hipStream_t st) {
+  GemmArgs a = gemm_common(d);
+  a.act = act;
+  a.act_scales = act_scales;
+  a.gather = gather;
+  a.gather_div = d->k;
+  a.w0 = wg;
+  a.w1 = wu;
+  a.s0 = sg;
+  a.s1 = su;
+  a.K = d->H;
+  a.N = d->I;
+  a.out = h;
+  a.out_scales = hs;
+  a.out_f32 = d->w_dtype == MOE_DT_F32;
+  a.sched = sched;
+  a.offsets = offsets;
+  StageTimer tm(MOE_STAGE_GATE_UP, st);
+  hipError_t e;
+  const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
+  if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
+  else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
+  else e = launch_gate_up_fp8(a, grid, st);
+  MOE_TRY_HIP(e, "gate/up launch");
+  return MOE_OK;
+}
+
+moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int32_t* offsets,
+                    const void* wd, const void* sd, void* y, const Schedule* sched, hipStream_t st) {
+  GemmArgs a = gemm_common(d);
+  a.act = h;
+  a.act_scales = hs;
+  a.w0 = wd;
+  a.s0 = sd;
+  a.K = d->I;
+  a.N = d->H;
+  a.out = y;
+  a.out_f32 = d->y_dtype == MOE_DT_F32;
+  a.sched = sched;
+  a.offsets = offsets;
+  StageTimer tm(MOE_STAGE_DOWN, st);
+  hipError_t e;
+  const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
+  if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
+  else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);
+  else e = launch_down_fp8(a, grid, st);
+  MOE_TRY_HIP(e, "down launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported combination";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+size_t moe_workspace_bytes(const moe_desc* d, int op) {
+  if (validate(d) != MOE_OK) return 0;
+  return ws_size(d, op);
+}
+
+moe_status moe_route_topk(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                          int32_t* ids, float* w, void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !w_router || !ids || !w) return fail(MOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(w_router)) return fail(MOE_EINVAL, "x and w_router must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  StageTimer tm(MOE_STAGE_ROUTE, st);
+  MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, d->H, d->E, d->k, d->act_dtype == MOE_DT_BF16,
+                                d->score, d->renormalize, d->routed_scale, ids, w, st),
+              "router launch");
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_desc* d, const int32_t* ids, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, void* x_sorted,
+                       float* x_sorted_scales, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (!counts || !offsets) return fail(MOE_EINVAL, "counts and offsets are required");
+  const int64_t P = pairs(d);
+  if (P > 0 && (!ids || !perm || !inv)) return fail(MOE_EINVAL, "ids, perm and inv are required");
+  if ((x == nullptr) != (x_sorted == nullptr)) return fail(MOE_EINVAL, "x and x_sorted go together");
+  if (x_sorted && is_fp8(d) && !x_sorted_scales)
+    return fail(MOE_EINVAL, "fp8 experts need x_sorted_scales with x_sorted");
+  if (x && (!aligned16(x) || !aligned16(x_sorted))) return fail(MOE_EINVAL, "x, x_sorted must be 16-byte aligned");
+  if ((s = check_ws(d, MOE_OP_PERMUTE, ws, ws_bytes)) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Carve c{(uint8_t*)ws};
+  PermuteWs pw = carve_permute(c, d, is_fp8(d));
+  SchedRequest none{};
+  if ((s = run_permute(d, ids, counts, offsets, perm, inv, nullptr, pw, none, none, st)) != MOE_OK) return s;
+  if (x_sorted && P > 0) {
+    if (is_fp8(d)) {
+      {
+        StageTimer tm(MOE_STAGE_QUANT_X, st);
+        MOE_TRY_HIP(launch_quant_rows_fp8((const uint16_t*)x, d->T, d->H, pw.xq, pw.xs, st), "quantize launch");
+      }
+      MOE_TRY_HIP(launch_gather_rows(pw.xq, perm, d->k, P, d->H, x_sorted, st), "gather launch");
+      MOE_TRY_HIP(launch_gather_scales(pw.xs, perm, d->k, P, d->H / 128, x_sorted_scales, st),
+                  "gather launch");
+    } else {
+      MOE_TRY_HIP(launch_gather_rows(x, perm, d->k, P, (int64_t)d->H * elt_bytes(d->act_dtype), x_sorted, st),
+                  "gather launch");
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status moe_expert_gate_up_swiglu(const moe_desc* d, const void* x_sorted, const float* x_scales,
+                                     const int32_t* offsets, const void* w_gate, const void* w_up,
+                                     const void* w_gate_scales, const void* w_up_scales, void* h,
+                                     float* h_scales, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (pairs(d) == 0) return MOE_OK;
+  if (!x_sorted || !offsets || !w_gate || !w_up || !h) return fail(MOE_EINVAL, "NULL tensor argument");
+  if (is_fp8(d) && (!x_scales || !w_gate_scales || !w_up_scales || !h_scales))
+    return fail(MOE_EINVAL, "fp8 experts need x_scales, weight scales and h_scales");
+  if (!aligned16(x_sorted) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h))
+    return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
+  if ((s = check_ws(d, MOE_OP_GATE_UP, ws, ws_bytes)) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Schedule* sched = nullptr;
+  if (d->w_dtype != MOE_DT_F32) {
+    sched = (Schedule*)ws;
+    MOE_TRY_HIP(launch_schedule(offsets, d->E, sched_req(sched, d, gate_up_ntiles(d)), st), "schedule launch");
+  }
+  return run_gate_up(d, x_sorted, x_scales, nullptr, offsets, w_gate, w_up, w_gate_scales, w_up_scales, h,
+                     h_scales, sched, st);
+}
+
+moe_status moe_expert_down(const moe_desc* d, const void* h, const float* h_scales, const int32_t* offsets,
+                           const void* w_down, const void* w_down_scales, void* y_sorted, void* ws,
+                           size_t ws_bytes, void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (pairs(d) == 0) return MOE_OK;
+  if (!h || !offsets || !w_down || !y_sorted) return fail(MOE_EINVAL, "NULL tensor argument");
+  if (is_fp8(d) && (!h_scales || !w_down_scales)) return fail(MOE_EINVAL, "fp8 experts need h_scales and w_down_scales");
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(y_sorted))
+    return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
+  if ((s = check_ws(d, MOE_OP_DOWN, ws, ws_bytes)) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Schedule* sched = nullptr;
+  if (d->w_dtype != MOE_DT_F32) {
+    sched = (Schedule*)ws;
+    MOE_TRY_HIP(launch_schedule(offsets, d->E, sched_req(sched, d, down_ntiles(d)), st), "schedule launch");
+  }
+  return run_down(d, h, h_scales, offsets, w_down, w_down_scales, y_sorted, sched, st);
+}
+
+moe_status moe_unpermute_combine(const moe_desc* d, const void* y_sorted, const int32_t* inv,
+                                 const float* topk_w, void* out, void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (d->T == 0) return MOE_OK;
+  if (!y_sorted || !inv || !topk_w || !out) return fail(MOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(y_sorted) || !aligned16(out)) return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  StageTimer tm(MOE_STAGE_COMBINE, st);
+  MOE_TRY_HIP(launch_combine(y_sorted, d->y_dtype == MOE_DT_F32, inv, topk_w, d->T, d->k, d->H, out,
+                             d->act_dtype == MOE_DT_F32, st),
+              "combine launch");
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                       const void* w_gate, const void* w_up, const void* w_down, const void* sg,
+                       const void* su, const void* sd, void* out, int32_t* ids_out, float* w_out,
+                       int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if ((s = check_ws(d, MOE_OP_FORWARD, ws, ws_bytes)) != MOE_OK) return s;
+  if (d->T > 0) {
+    if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return fail(MOE_EINVAL, "NULL tensor argument");
+    if (is_fp8(d) && (!sg || !su || !sd)) return fail(MOE_EINVAL, "fp8 experts need all three block-scale tensors");
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned16(out))
+      return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  Carve c{(uint8_t*)ws};
+  ForwardWs fw = carve_forward(c, d);
+  int32_t* ids = ids_out ? ids_out : fw.ids;
+  float* w = w_out ? w_out : fw.w;
+  int32_t* counts = counts_out ? counts_out : fw.counts;
+  const int64_t P = pairs(d);
+
+  if (d->T > 0) {
+    StageTimer tm(MOE_STAGE_ROUTE, st);
+    MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, d->H, d->E, d->k, d->act_dtype == MOE_DT_BF16,
+                                  d->score, d->renormalize, d->routed_scale, ids, w, st),
+                "router launch");
+  }
+  SchedRequest sgu{}, sdn{};
+  if (d->w_dtype != MOE_DT_F32) {
+    sgu = sched_req(fw.sched_gu, d, gate_up_ntiles(d));
+    sdn = sched_req(fw.sched_dn, d, down_ntiles(d));
+  }
+  if ((s = run_permute(d, ids, counts, fw.offsets, fw.perm, fw.inv, fw.touched, fw.pw, sgu, sdn, st)) != MOE_OK)
+    return s;
+  if (P == 0) return MOE_OK;
+  const void* act = x;
+  const float* act_scales = nullptr;
+  if (is_fp8(d)) {
+    StageTimer tm(MOE_STAGE_QUANT_X, st);
+    MOE_TRY_HIP(launch_quant_rows_fp8((const uint16_t*)x, d->T, d->H, fw.pw.xq, fw.pw.xs, st), "quantize launch");
+    act = fw.pw.xq;
+    act_scales = fw.pw.xs;
+  }
+  if ((s = run_gate_up(d, act, act_scales, fw.perm, fw.offsets, w_gate, w_up, sg, su, fw.h, fw.hs, fw.sched_gu,
+                       st)) != MOE_OK)
+    return s;
+  if ((s = run_down(d, fw.h, fw.hs, fw.offsets, w_down, sd, fw.y, fw.sched_dn, st)) != MOE_OK) return s;
+  {
+    StageTimer tm(MOE_STAGE_COMBINE, st);
+    MOE_TRY_HIP(launch_combine(fw.y, d->y_dtype == MOE_DT_F32, fw.inv, w, d->T, d->k, d->H, out,
+                               d->act_dtype == MOE_DT_F32, st),
+                "combine launch");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_timing_enable(int on) {
+  g_timing = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(double* ms, int64_t* launches) {
+  if (!ms || !launches) return fail(MOE_EINVAL, "NULL output");
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  moe_status result = MOE_OK;
+  for (auto& p : g_pending) {
+    float t = 0.f;
+    if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&t, p.start, p.stop) != hipSuccess)
+      result = fail(MOE_EHIP, "event timing failed");
+    ms[p.stage] += t;
+    launches[p.stage] += 1;
+    g_event_pool.push_back(p.start);
+    g_event_pool.push_back(p.stop);
+  }
+  g_pending.clear();
+  return result;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Device-side helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;      // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 32;
+
+// One unit of grouped-GEMM work: rows [row_begin, row_end) of the expert-sorted
+// matrix, all owned by `expert`, times output-channel tile `ntile`.
+struct WorkItem {
+  int32_t row_begin;
+  int32_t row_end;
+  int32_t expert;
+  int32_t ntile;
+};
+
+// Schedule header in the workspace, followed by WorkItem items[capacity].
+struct Schedule {
+  int32_t total;
+  int32_t pad[3];
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// value of an E8M0 scale byte: 2^(b-127)
+__device__ __forceinline__ float e8m0_to_f32(uint8_t b) { return __builtin_ldexpf(1.0f, (int)b - 127); }
+
+// Packs two floats into OCP e4m3 codes (round to nearest even); inputs are
+// within +-464 by construction, so no code overflows.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// The XCD-aware work index of this workgroup: consecutive work items land on
+// the same XCD (and its L2), the XCDs split the items into contiguous ranges.
+// Returns -1 for workgroups beyond the live work.  gridDim.x is a multiple of 8.
+__device__ __forceinline__ int xcd_work_index(int total) {
+  int xcd = blockIdx.x % kNumXcd;
+  int slot = blockIdx.x / kNumXcd;
+  int per = (total + kNumXcd - 1) / kNumXcd;
+  if (slot >= per) return -1;
+  int w = xcd * per + slot;
+  return w < total ? w : -1;
+}
+
+}  // namespace moe

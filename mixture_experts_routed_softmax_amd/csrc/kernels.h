@@ -1,0 +1,89 @@
+// Host-side launchers of the libmoe kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct WorkItem;
+struct Schedule;
+
+// ---- router
+hipError_t launch_route_topk(const void* x, const void* w_router, const float* bias, int64_t T,
+                             int H, int E, int k, int act_bf16, int score, int renorm,
+                             float routed_scale, int32_t* ids, float* w, hipStream_t stream);
+
+// ---- permutation
+constexpr int kPermChunk = 1024;   // (token, slot) pairs per histogram / scatter block
+
+inline int64_t perm_blocks(int64_t P) { return (P + kPermChunk - 1) / kPermChunk; }
+
+// One grouped-GEMM schedule to be built by the scan kernel.
+struct SchedRequest {
+  Schedule* sched;    // header + items, or nullptr
+  int rows_per_tile;  // BM (token rows per tile)
+  int ntiles;         // output-channel tiles per expert
+  int capacity;       // items the buffer holds
+};
+
+hipError_t launch_hist(const int32_t* ids, int64_t P, int E, int32_t* block_counts,
+                       hipStream_t stream);
+// counts, offsets, block bases, touched-expert list and up to two schedules.
+hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* block_base, int32_t* touched,
+                       SchedRequest s0, SchedRequest s1, hipStream_t stream);
+hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* block_base,
+                          int32_t* perm, int32_t* inv, hipStream_t stream);
+// schedule from offsets alone (staged entry points)
+hipError_t launch_schedule(const int32_t* offsets, int E, SchedRequest s, hipStream_t stream);
+
+// gather rows: dst[r] = src[perm[r] / k]  (row_bytes multiple of 16)
+hipError_t launch_gather_rows(const void* src, const int32_t* perm, int k, int64_t P,
+                              int64_t row_bytes, void* dst, hipStream_t stream);
+// gather fp32 scale rows: dst[r, :] = src[perm[r] / k, :]
+hipError_t launch_gather_scales(const float* src, const int32_t* perm, int k, int64_t P, int n,
+                                float* dst, hipStream_t stream);
+
+// ---- fp8 activation quantization (per row, per 128 channels)
+hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int64_t rows, int n, uint8_t* codes,
+                                 float* scales, hipStream_t stream);
+
+// ---- grouped GEMMs
+struct GemmArgs {
+  const void* act;          // activation rows
+  const float* act_scales;  // fp8: [rows_src, K/128]
+  const int32_t* gather;    // nullptr, or sorted row -> perm entry (token = entry / gather_div)
+  int gather_div;
+  const void* w0;           // gate (or down) weights
+  const void* w1;           // up weights (gate/up only)
+  const void* s0;           // fp8 block scales of w0
+  const void* s1;           // fp8 block scales of w1
+  int scale_ue8m0;
+  int K;                    // reduction length
+  int N;                    // output channels (I for gate/up, H for down)
+  void* out;                // [P, N]
+  float* out_scales;        // fp8 h: [P, N/128]
+  int out_f32;              // 1: fp32 output rows, 0: bf16
+  const Schedule* sched;
+  const int32_t* offsets;   // f32 path: expert of a row
+  int E;
+  int64_t P;
+};
+
+// tile geometry of the grouped GEMMs
+constexpr int kGemmRowsPerTile = 128;   // token rows per tile
+constexpr int kGemmGateUpChannels = 128; // h channels per gate/up tile (256 weight rows)
+constexpr int kGemmDownChannels = 256;   // output channels per down tile
+
+hipError_t launch_gate_up_bf16(const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_down_bf16(const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_gate_up_fp8(const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_down_fp8(const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_down_f32(const GemmArgs& a, hipStream_t stream);
+
+// ---- combine
+hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const float* w, int64_t T,
+                          int k, int H, void* out, int out_f32, hipStream_t stream);
+
+}  // namespace moe

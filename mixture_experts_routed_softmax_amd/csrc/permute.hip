@@ -1,0 +1,301 @@
+// Ordering (token, slot) pairs by selected expert, and the row gathers.
+//
+// "Experts backends", backend table, rows grouped_mm and deepgemm: tokens are
+// ordered (sorted) by their selected expert so that all experts run as one
+// grouped GEMM.  The order inside an expert is ascending (token, slot), i.e. a
+// stable counting sort of the flattened top-k ids:
+//   counts[e]  = #{p : ids[p] == e}
+//   offsets[e] = sum_{e' < e} counts[e']            (E+1 entries)
+//   row(p)     = offsets[ids[p]] + #{p' < p : ids[p'] == ids[p]}
+//   perm[row(p)] = p,  inv[p] = row(p)
+// Three launches, no atomics on global memory and no host synchronisation:
+//   hist    : per-chunk expert histograms (chunks of 1024 pairs)
+//   scan    : counts, offsets, per-chunk bases (offsets + earlier chunks), the
+//             touched-expert list and the grouped-GEMM work schedules
+//   scatter : stable in-chunk ranks (wave readlane scan + per-wave counts)
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                   int E, int32_t* __restrict__ block_counts) {
+  __shared__ int s_hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kPermChunk;
+#pragma unroll
+  for (int q = 0; q < kPermChunk / 256; ++q) {
+    int64_t p = base + q * 256 + threadIdx.x;
+    if (p < P) {
+      const int e = ids[p];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&s_hist[e], 1);   // out-of-range ids are ignored
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    block_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
+}
+
+// In-place exclusive scan of v[0..n) (n <= 1024) by the whole 1024-thread block;
+// returns the total.  v must be in LDS; tmp is LDS scratch of 1024 ints.
+__device__ int block_exclusive_scan(int* v, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  tmp[tid] = tid < n ? v[tid] : 0;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int add = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  int total = tmp[1023];
+  if (tid < n) v[tid] = tmp[tid] - v[tid];
+  __syncthreads();
+  return total;
+}
+
+// Fill one schedule: experts in ascending order, then output-channel tiles,
+// then row tiles (fastest), so that consecutive work items share weights.
+__device__ void build_schedule(const int* s_offsets, int E, SchedRequest rq, int* s_tiles,
+                               int* s_items, int* s_tmp) {
+  const int tid = threadIdx.x;
+  const int BM = rq.rows_per_tile;
+  for (int e = tid; e < E; e += 1024) {
+    int c = s_offsets[e + 1] - s_offsets[e];
+    s_tiles[e] = (c + BM - 1) / BM;
+    s_items[e] = s_tiles[e] * rq.ntiles;
+  }
+  __syncthreads();
+  int total = block_exclusive_scan(s_items, E, s_tmp);   // s_items -> item bases
+  if (tid == 0) {
+    s_items[E] = total;
+    rq.sched->total = total;
+  }
+  __syncthreads();
+  WorkItem* items = (WorkItem*)(rq.sched + 1);
+  for (int idx = tid; idx < total; idx += 1024) {
+    // largest e with base[e] <= idx
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_items[mid] <= idx) lo = mid; else hi = mid - 1;
+    }
+    int e = lo;
+    int local = idx - s_items[e];
+    int nt = local / s_tiles[e];
+    int mt = local - nt * s_tiles[e];
+    int rb = s_offsets[e] + mt * BM;
+    int re = min(rb + BM, s_offsets[e + 1]);
+    items[idx] = WorkItem{rb, re, e, nt};
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(
+    const int32_t* __restrict__ block_counts, int64_t nblocks, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ block_base, int32_t* __restrict__ touched,
+    SchedRequest s0, SchedRequest s1) {
+  __shared__ int s_part[4][kMaxExperts];
+  __shared__ int s_offsets[kMaxExperts + 1];
+  __shared__ int s_tiles[kMaxExperts];
+  __shared__ int s_items[kMaxExperts + 1];
+  __shared__ int s_tmp[1024];
+  const int tid = threadIdx.x;
+  const int e = tid & 255;
+  const int part = tid >> 8;
+  const int64_t per = (nblocks + 3) / 4;
+  const int64_t b0 = part * per;
+  const int64_t b1 = min(nblocks, b0 + per);
+  int sum = 0;
+  if (e < E)
+    for (int64_t b = b0; b < b1; ++b) sum += block_counts[b * E + e];
+  s_part[part][e] = sum;
+  __syncthreads();
+  if (tid < E) {
+    int c = s_part[0][tid] + s_part[1][tid] + s_part[2][tid] + s_part[3][tid];
+    s_offsets[tid] = c;
+    counts[tid] = c;
+  }
+  __syncthreads();
+  int total = block_exclusive_scan(s_offsets, E, s_tmp);
+  if (tid == 0) s_offsets[E] = total;
+  __syncthreads();
+  for (int i = tid; i <= E; i += 1024) offsets[i] = s_offsets[i];
+  // per-chunk bases
+  if (e < E) {
+    int run = s_offsets[e];
+    for (int p = 0; p < part; ++p) run += s_part[p][e];
+    for (int64_t b = b0; b < b1; ++b) {
+      int c = block_counts[b * E + e];
+      block_base[b * E + e] = run;
+      run += c;
+    }
+  }
+  // touched experts, ascending, count in touched[E]
+  if (touched != nullptr) {
+    if (tid < E) s_tiles[tid] = (s_offsets[tid + 1] - s_offsets[tid]) > 0 ? 1 : 0;
+    __syncthreads();
+    int U = block_exclusive_scan(s_tiles, E, s_tmp);
+    if (tid < E && s_offsets[tid + 1] > s_offsets[tid]) touched[s_tiles[tid]] = tid;
+    if (tid == 0) touched[E] = U;
+    __syncthreads();
+  }
+  if (s0.sched != nullptr) build_schedule(s_offsets, E, s0, s_tiles, s_items, s_tmp);
+  if (s1.sched != nullptr) build_schedule(s_offsets, E, s1, s_tiles, s_items, s_tmp);
+}
+
+__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
+                                                        SchedRequest rq) {
+  __shared__ int s_offsets[kMaxExperts + 1];
+  __shared__ int s_tiles[kMaxExperts];
+  __shared__ int s_items[kMaxExperts + 1];
+  __shared__ int s_tmp[1024];
+  for (int i = threadIdx.x; i <= E; i += 1024) s_offsets[i] = offsets[i];
+  __syncthreads();
+  build_schedule(s_offsets, E, rq, s_tiles, s_items, s_tmp);
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                      int E, const int32_t* __restrict__ block_base,
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ inv) {
+  __shared__ int s_cursor[kMaxExperts];
+  __shared__ int s_wcount[4][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 256) {
+    s_cursor[e] = block_base[(int64_t)blockIdx.x * E + e];
+    s_wcount[0][e] = s_wcount[1][e] = s_wcount[2][e] = s_wcount[3][e] = 0;
+  }
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  for (int round = 0; round < kPermChunk / 256; ++round) {
+    const int64_t p = base + round * 256 + tid;
+    int e = p < P ? ids[p] : -1;
+    if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
+    const bool valid = e >= 0;
+    // rank among earlier lanes of this wave with the same expert
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      int ej = __builtin_amdgcn_readlane(e, j);
+      rank += (j < lane && ej == e) ? 1 : 0;
+    }
+    if (valid) atomicAdd(&s_wcount[wave][e], 1);
+    __syncthreads();
+    if (valid) {
+      int row = s_cursor[e] + rank;
+      for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
+      perm[row] = (int32_t)p;
+      inv[p] = row;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += 256) {
+      s_cursor[x] += s_wcount[0][x] + s_wcount[1][x] + s_wcount[2][x] + s_wcount[3][x];
+      s_wcount[0][x] = s_wcount[1][x] = s_wcount[2][x] = s_wcount[3][x] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src,
+                                                          const int32_t* __restrict__ perm, int k,
+                                                          int64_t row_bytes, uint8_t* __restrict__ dst) {
+  const int64_t r = blockIdx.x;
+  const int64_t t = perm[r] / k;
+  const i32x4* s = (const i32x4*)(src + t * row_bytes);
+  i32x4* d = (i32x4*)(dst + r * row_bytes);
+  for (int64_t c = threadIdx.x; c < row_bytes / 16; c += 256) d[c] = s[c];
+}
+
+__global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restrict__ src,
+                                                            const int32_t* __restrict__ perm, int k,
+                                                            int64_t P, int n, float* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= P * n) return;
+  const int64_t r = i / n;
+  const int c = (int)(i % n);
+  dst[i] = src[(int64_t)(perm[r] / k) * n + c];
+}
+
+// Dynamic fp8 quantization of bf16 rows, per 128 channels: s = amax/448,
+// code = RNE_e4m3(x/s); amax = 0 gives s = 1 and zero codes.
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __restrict__ x,
+                                                             int n, uint8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int groups = n / 128;
+  for (int g = wave; g < groups; g += 4) {
+    const uint32_t two = *(const uint32_t*)(x + row * n + g * 128 + 2 * lane);
+    float a = bf16_bits_to_f32((uint16_t)(two & 0xffff));
+    float b = bf16_bits_to_f32((uint16_t)(two >> 16));
+    float m = fmaxf(fabsf(a), fabsf(b));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float s = m > 0.f ? m / 448.0f : 1.0f;
+    uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(a / s, b / s, 0, false);
+    *(uint16_t*)(codes + row * n + g * 128 + 2 * lane) = (uint16_t)(pk & 0xffff);
+    if (lane == 0) scales[row * groups + g] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hist(const int32_t* ids, int64_t P, int E, int32_t* block_counts,
+                       hipStream_t stream) {
+  int64_t nb = perm_blocks(P);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nb), dim3(256), 0, stream, ids, P, E, block_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* block_base, int32_t* touched, SchedRequest s0,
+                       SchedRequest s1, hipStream_t stream) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, block_counts, nblocks, E, counts,
+                     offsets, block_base, touched, s0, s1);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* block_base,
+                          int32_t* perm, int32_t* inv, hipStream_t stream) {
+  int64_t nb = perm_blocks(P);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(256), 0, stream, ids, P, E,
+                     block_base, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const int32_t* offsets, int E, SchedRequest s, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, const int32_t* perm, int k, int64_t P,
+                              int64_t row_bytes, void* dst, hipStream_t stream) {
+  if (P == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)P), dim3(256), 0, stream,
+                     (const uint8_t*)src, perm, k, row_bytes, (uint8_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_scales(const float* src, const int32_t* perm, int k, int64_t P, int n,
+                                float* dst, hipStream_t stream) {
+  if (P == 0) return hipSuccess;
+  int64_t total = P * n;
+  hipLaunchKernelGGL(gather_scales_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, src, perm, k, P, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int64_t rows, int n, uint8_t* codes,
+                                 float* scales, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x_bf16, n,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

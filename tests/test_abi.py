@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, and rejects bad requests on the host before launching
+anything (the "Experts backends" page's fail-loudly conventions: static
+activation quantization is rejected, unsupported setups raise instead of
+corrupting output)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import mixture_experts_routed_softmax_amd as moe
+
+
+def test_header_symbols_exported():
+    names = moe.exported_symbols_of_header()
+    for required in ("moe_route_topk", "moe_permute", "moe_expert_gate_up_swiglu",
+                     "moe_expert_down", "moe_unpermute_combine", "moe_forward",
+                     "moe_workspace_bytes", "moe_status_str", "moe_last_error",
+                     "moe_timing_enable", "moe_timing_read"):
+        assert required in names
+    lib = moe.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_desc_layout_matches_header(tmp_path):
+    # compile a C probe against include/moe.h and compare every field offset
+    fields = [f[0] for f in moe.MoeDesc._fields_]
+    src = tmp_path / "probe.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\nint main(void){\n'
+                   + "".join('printf("%%zu\\n", offsetof(moe_desc, %s));\n' % f for f in fields)
+                   + 'printf("%zu\\n", sizeof(moe_desc));return 0;}\n')
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.dirname(moe.HEADER_PATH), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [getattr(moe.MoeDesc, f).offset for f in fields] + [ctypes.sizeof(moe.MoeDesc)]
+    assert got == want
+
+
+def _qwen(**kw):
+    base = dict(score="softmax", renormalize=False, routed_scale=1.0, act_dtype="bf16", w_dtype="bf16")
+    base.update(kw)
+    return moe.make_desc(4096, 2048, 1408, 60, 4, **base)
+
+
+def _ds_fp8(**kw):
+    base = dict(score="sigmoid", renormalize=True, routed_scale=2.5, act_dtype="bf16", w_dtype="fp8",
+                w_scale_fmt="f32")
+    base.update(kw)
+    return moe.make_desc(8192, 7168, 2048, 256, 8, **base)
+
+
+def _status_of(fn, *args):
+    with pytest.raises(moe.MoeError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+def _forward_nulls(desc, ws=None):
+    moe.moe_forward(desc, None, None, None, None, None, None, None, None, None, None, ws=ws, stream=0)
+
+
+def test_status_strings():
+    assert moe.moe_status_str(moe.MOE_OK) == "MOE_OK"
+    assert "workspace" in moe.moe_status_str(moe.MOE_EWORKSPACE)
+    assert "unknown" in moe.moe_status_str(99)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(k=0), moe.MOE_EINVAL),
+    (dict(k=61), moe.MOE_EINVAL),
+    (dict(E=257, k=4), moe.MOE_EINVAL),
+    (dict(H=2000), moe.MOE_EUNSUPPORTED),        # bf16 K not a multiple of 64
+    (dict(T=-1), moe.MOE_EINVAL),
+    (dict(act_dtype=7), moe.MOE_EINVAL),
+    (dict(score=5), moe.MOE_EINVAL),
+    (dict(renormalize=2), moe.MOE_EINVAL),
+    (dict(w_scale_fmt=moe.MOE_SCALE_F32), moe.MOE_EINVAL),   # scales on bf16 experts
+    (dict(act_dtype=moe.MOE_DT_F32), moe.MOE_EUNSUPPORTED),  # f32 x with bf16 experts
+    (dict(reserved=1), moe.MOE_EINVAL),
+    (dict(k=33, E=64), moe.MOE_EUNSUPPORTED),
+])
+def test_validation_rejects(bad, status):
+    d = _qwen()
+    for key, v in bad.items():
+        if key == "reserved":
+            d.reserved[0] = v
+        else:
+            setattr(d, key, v)
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_FORWARD) == 0
+    assert _status_of(_forward_nulls, d) == status
+    assert moe.moe_last_error() != ""
+
+
+def test_fp8_static_activation_rejected():
+    d = _ds_fp8(act_scheme="static")
+    assert _status_of(_forward_nulls, d) == moe.MOE_EUNSUPPORTED
+    assert "static" in moe.moe_last_error()
+
+
+@pytest.mark.parametrize("bad", [dict(block=64), dict(H=7168 + 64)])
+def test_fp8_geometry_rejected(bad):
+    d = _ds_fp8()
+    for key, v in bad.items():
+        setattr(d, key, v)
+    assert _status_of(_forward_nulls, d) == moe.MOE_EUNSUPPORTED
+
+
+def test_fp8_needs_scales_format():
+    d = _ds_fp8(w_scale_fmt="none")
+    assert _status_of(_forward_nulls, d) == moe.MOE_EINVAL
+
+
+def test_workspace_required_and_sized():
+    d = _qwen()
+    need = moe.moe_workspace_bytes(d, moe.MOE_OP_FORWARD)
+    # the workspace holds at least h [P,I] bf16 and y [P,H] bf16
+    P = 4096 * 4
+    assert need >= P * 1408 * 2 + P * 2048 * 2
+    assert _status_of(_forward_nulls, d) == moe.MOE_EWORKSPACE
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_ROUTE) == 0
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_PERMUTE) > 0
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_GATE_UP) > 0
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_DOWN) > 0
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_COMBINE) == 0
+    # fp8 workspaces also hold the quantized activations
+    f = _ds_fp8()
+    assert moe.moe_workspace_bytes(f, moe.MOE_OP_PERMUTE) >= 8192 * 7168
+
+
+def test_null_tensors_rejected_before_launch():
+    d = moe.make_desc(16, 2048, 1408, 60, 4)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_topk(d, None, None, None, None, None, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL
+
+
+def test_empty_route_is_noop():
+    d = moe.make_desc(0, 2048, 1408, 60, 4)
+    moe.moe_route_topk(d, None, None, None, None, None, stream=0)
+
+
+def test_stream_path_reported_unsupported_until_built():
+    d = _qwen(path="stream")
+    st = _status_of(_forward_nulls, d)
+    assert st in (moe.MOE_EUNSUPPORTED, moe.MOE_EWORKSPACE)
