@@ -1,0 +1,232 @@
+"""Throughput of the routed mixture-of-experts layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T N]
+                    [--scale-fmt f32|ue8m0] [--no-cpu-baseline]
+
+A step is one moe_forward call (router, permutation, gate/up + SwiGLU, down,
+combine) over one batch of T synthetic tokens whose inputs and weights are
+already resident in HBM.  W untimed warmup steps are followed by exactly K
+timed steps, bracketed by torch.cuda.synchronize(); value = T * K / elapsed.
+
+The default workload is the Qwen1.5-MoE-A2.7B-like prefill layer (T=4096,
+H=2048, I=1408, E=60, top-4 softmax without renormalisation, Zipf-skewed
+router bias, bf16).  Other workloads (--config) print the same line for
+measurement.  The JSON line also carries:
+
+* roofline: the gate/up grouped GEMM (two thirds of the layer's FLOPs) for
+  prefill workloads, priced at its algorithmic FLOPs 2*P*H*2I against the dense
+  MFMA peak of its dtype; for decode workloads (T <= 64) the whole layer's
+  touched-expert weight bytes against 8 TB/s.  Kernel durations come from HIP
+  events the library records around each of its launches on the caller's
+  stream during the timed steps.
+* cpu_baseline: the fp64 oracle (never tuned) on the host cores, on a bounded
+  sample: the router over all T tokens plus the expert MLPs and the combine on
+  a sample of tokens sized to about 10 s; tokens/s = 1 / (router time per
+  token + expert time per token).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+METRIC = "MoE-layer tokens/s; % MFMA peak (prefill), % HBM BW (decode)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="qwen_prefill",
+                   choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8"])
+    p.add_argument("--T", type=int, default=None)
+    p.add_argument("--scale-fmt", default="f32", choices=["f32", "ue8m0"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(s, L, budget_s: float):
+    """Time the fp64 oracle on a bounded sample of this workload."""
+    import numpy as np
+    import oracle
+
+    hl = {k: (None if v is None else v.detach().cpu()) for k, v in L.items()}
+    score = oracle.SOFTMAX if s.score == "softmax" else oracle.SIGMOID
+    t0 = time.perf_counter()
+    ids, w = oracle.route(hl["x"], hl["w_router"], hl["router_bias"], s.k, score, s.renormalize,
+                          s.routed_scale)
+    t_route = time.perf_counter() - t0
+    if s.experts == "fp8":
+        fmt = oracle.SCALE_UE8M0 if s.scale_fmt == "ue8m0" else oracle.SCALE_F32
+        ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], hl["s_gate"], hl["s_up"],
+                            hl["s_down"], fmt, s.block, act_fp8=True)
+    else:
+        ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"])
+    rng = np.random.default_rng(0)
+    order = rng.permutation(s.T)
+    n, t_exp, done = 8, 0.0, 0
+    while done < s.T:
+        batch = order[done:done + n]
+        t0 = time.perf_counter()
+        ex.combine(hl["x"], ids, w, batch)
+        t_exp += time.perf_counter() - t0
+        done += batch.size
+        if t_exp + t_route >= budget_s:
+            break
+        per = t_exp / done
+        n = int(min(max(8, (budget_s - t_exp - t_route) / per), s.T - done))
+        if n <= 0:
+            break
+    per_token = t_route / s.T + t_exp / done
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "fp64 oracle: router on all %d tokens (%.2f s) + expert MLPs and combine on "
+                      "%d sampled tokens (%.2f s); tokens/s = 1/(router s/token + expert s/token)"
+                      % (s.T, t_route, done, t_exp)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_routed_softmax_amd as moe
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    over = {}
+    if args.T is not None:
+        over["T"] = args.T
+    if args.config == "dsv3_fp8":
+        over["scale_fmt"] = args.scale_fmt
+    s = synthetic.spec(args.config, **over)
+    log("workload %s T=%d H=%d I=%d E=%d k=%d experts=%s" % (s.name, s.T, s.H, s.I, s.E, s.k, s.experts))
+    t0 = time.perf_counter()
+    L = synthetic.make_layer(s, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+
+    d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,
+                      routed_scale=s.routed_scale, act_dtype=s.act, w_dtype=s.experts,
+                      w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none")
+    out = torch.empty(s.T, s.H, dtype=torch.float32 if s.act == "f32" else torch.bfloat16, device=dev)
+    counts = torch.empty(s.E, dtype=torch.int32, device=dev)
+    ws = moe.workspace(d, moe.MOE_OP_FORWARD, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"],
+                        L["w_down"], L.get("s_gate"), L.get("s_up"), L.get("s_down"), out, None, None,
+                        counts, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    decode = s.T <= 64
+    flush = None
+    if decode:
+        # touched weights of a decode step fit the 256 MB last-level cache: evict it
+        # between timed steps by rewriting a 2 GiB buffer (outside the timed events)
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    moe.moe_timing_enable(True)
+    moe.moe_timing_read()
+    if decode:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            flush.zero_()
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        times = sorted(a.elapsed_time(b) for a, b in ev)
+        elapsed_ms = sum(times)
+        ms_per_step = times[len(times) // 2]
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed_ms = (time.perf_counter() - t0) * 1e3
+        ms_per_step = elapsed_ms / args.steps
+    stages = moe.moe_timing_read()
+    moe.moe_timing_enable(False)
+    value = s.T / (ms_per_step / 1e3)
+    for name, (ms, n) in stages.items():
+        if n:
+            log("  stage %-8s %8.1f us/launch  (%d launches)" % (name, 1e3 * ms / n, n))
+
+    P = s.T * s.k
+    cnt = counts.cpu()
+    touched = int((cnt > 0).sum())
+    wbytes_per_expert = 3 * s.H * s.I * (1 if s.experts == "fp8" else (4 if s.experts == "f32" else 2))
+    if decode:
+        # HBM roofline of the whole step: weights of the touched experts only
+        alg_bytes = touched * wbytes_per_expert
+        achieved = alg_bytes / (ms_per_step / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "moe_forward (whole step, median of %d individually timed steps)" % args.steps,
+                "alg_bytes_per_launch": alg_bytes, "touched_experts": touched}
+    else:
+        ms_gu, n_gu = stages["gate_up"]
+        avg_ms = ms_gu / max(n_gu, 1)
+        flops = 2.0 * P * s.H * 2 * s.I
+        achieved = flops / (avg_ms / 1e3) / 1e12
+        peak = PEAK_TFLOPS[s.experts]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "gate_up grouped GEMM (%s)" % s.experts,
+                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": flops}
+    layer_flops = 2.0 * P * 3 * s.H * s.I
+    log("layer: %.3f ms/step, %.0f tokens/s, %.1f TFLOP/s expert GEMMs, touched %d/%d experts, "
+        "max/mean tokens per expert %d/%.1f"
+        % (ms_per_step, value, layer_flops / (ms_per_step / 1e3) / 1e12, touched, s.E, int(cnt.max()),
+           P / s.E))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del ws
+        cpu = cpu_baseline(s, L, args.cpu_seconds)
+        log("cpu baseline: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[s.experts], "data": "synthetic",
+        "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
+                   "experts": s.experts, "score": s.score, "renormalize": s.renormalize,
+                   "routed_scale": s.routed_scale, "router_bias": s.bias,
+                   **({"scale_fmt": s.scale_fmt} if s.experts == "fp8" else {}),
+                   "layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,64 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (moe_forward, default path).
+
+Routing and the permutation are checked for all tokens, bit for bit, against
+the oracle.  The expert outputs are checked on a coverage sample the oracle
+computes row by row: the tokens owning the first and last row of every
+non-empty expert segment (the ragged tail tiles) plus seeded random tokens.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from moe_cases import (coverage_tokens, host, oracle_experts, oracle_route, row_rel_err,
+                       run_forward, tol_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_case(s, seed, n_random, limit):
+    L = synthetic.make_layer(s, seed=seed, device="cuda")
+    out, ids, w, counts = run_forward(s, L)
+    hl = host(L)
+    del L
+    gc.collect()
+    torch.cuda.empty_cache()
+    ids_o, w_o = oracle_route(s, hl)
+    got_ids = ids.cpu().numpy()
+    assert np.array_equal(got_ids, ids_o), "router ids differ on %d of %d rows" % (
+        int((got_ids != ids_o).any(1).sum()), s.T)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=1e-5, atol=1e-7)
+    counts_o, offsets_o, perm_o, inv_o = oracle.permute(ids_o, s.E)
+    assert np.array_equal(counts.cpu().numpy(), counts_o)
+    toks = coverage_tokens(perm_o, offsets_o, s.k, n_random, seed=seed, limit=limit)
+    ex = oracle_experts(s, hl)
+    ref = ex.combine(hl["x"], ids_o, w_o, toks)
+    got = out[torch.from_numpy(toks).cuda()].cpu().float().numpy()
+    err = row_rel_err(got, ref)
+    print("%s T=%d: %d tokens checked, max row rel err %.3e (tol %.0e)" % (s.name, s.T, toks.size, err,
+                                                                           tol_of(s)))
+    assert err <= tol_of(s)
+
+
+def test_qwen_prefill_full():
+    _full_case(synthetic.spec("qwen_prefill"), seed=0, n_random=64, limit=None)
+
+
+@pytest.mark.parametrize("T", synthetic.TOKEN_COUNTS["qwen_decode"])
+def test_qwen_decode_full(T):
+    _full_case(synthetic.spec("qwen_decode", T=T), seed=T, n_random=T, limit=None)
+
+
+def test_dsv3_bf16_full():
+    _full_case(synthetic.spec("dsv3_bf16"), seed=0, n_random=32, limit=160)
+
+
+@pytest.mark.parametrize("T", synthetic.TOKEN_COUNTS["dsv3_fp8"])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_dsv3_fp8_full(T, fmt):
+    _full_case(synthetic.spec("dsv3_fp8", T=T, scale_fmt=fmt), seed=1, n_random=32,
+               limit=160 if T > 64 else 64)
