@@ -117,8 +117,14 @@ struct Carve {
   }
 };
 
-int gate_up_ntiles(const moe_desc* d) { return (d->I + kGemmGateUpChannels - 1) / kGemmGateUpChannels; }
-int down_ntiles(const moe_desc* d) { return (d->H + kGemmDownChannels - 1) / kGemmDownChannels; }
+int gate_up_ntiles(const moe_desc* d) {
+  const int c = d->w_dtype == MOE_DT_FP8_E4M3 ? kGemmGateUpChannelsFp8 : kGemmGateUpChannelsBf16;
+  return (d->I + c - 1) / c;
+}
+int down_ntiles(const moe_desc* d) {
+  const int c = d->w_dtype == MOE_DT_FP8_E4M3 ? kGemmDownChannelsFp8 : kGemmDownChannelsBf16;
+  return (d->H + c - 1) / c;
+}
 
 int64_t sched_capacity(const moe_desc* d, int ntiles) {
   const int64_t P = pairs(d);
@@ -128,7 +134,11 @@ int64_t sched_capacity(const moe_desc* d, int ntiles) {
 
 size_t sched_bytes(int64_t cap) { return sizeof(Schedule) + (size_t)cap * sizeof(WorkItem); }
 
-int grid_for(int64_t cap) { return (int)((cap + kNumXcd - 1) / kNumXcd * kNumXcd); }
+// grid covering every item index up to cap under xcd_work_index's mapping
+int grid_for(int64_t cap) {
+  const int64_t per = (int64_t)kNumXcd * kXcdChunk;
+  return (int)((cap + per - 1) / per * per);
+}
 
 struct PermuteWs {
   int32_t* block_counts;

@@ -56,15 +56,18 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// The XCD-aware work index of this workgroup: consecutive work items land on
-// the same XCD (and its L2), the XCDs split the items into contiguous ranges.
-// Returns -1 for workgroups beyond the live work.  gridDim.x is a multiple of 8.
+// XCD-aware work index of this workgroup.  Workgroups are dealt round-robin
+// to the 8 XCDs; work items are dealt to XCDs in chunks of kXcdChunk
+// consecutive items (consecutive items share an expert's weight tile, so a
+// chunk reuses it from one L2), and successive chunks go to successive XCDs
+// so that a hot expert's items spread over all of them.  Returns -1 for
+// workgroups beyond the live work.  gridDim.x is a multiple of
+// 8 * kXcdChunk covering every item index the schedule can hold.
+constexpr int kXcdChunk = 8;
 __device__ __forceinline__ int xcd_work_index(int total) {
-  int xcd = blockIdx.x % kNumXcd;
-  int slot = blockIdx.x / kNumXcd;
-  int per = (total + kNumXcd - 1) / kNumXcd;
-  if (slot >= per) return -1;
-  int w = xcd * per + slot;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int slot = blockIdx.x / kNumXcd;
+  const int w = ((slot / kXcdChunk) * kNumXcd + xcd) * kXcdChunk + slot % kXcdChunk;
   return w < total ? w : -1;
 }
 

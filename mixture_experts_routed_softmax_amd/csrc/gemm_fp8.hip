@@ -54,10 +54,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
     const uint8_t* src;
     int ch;
     if (kMode == 0) {
-      ch = it.ntile * kGemmGateUpChannels + (row & 127);
+      ch = it.ntile * kGemmGateUpChannelsFp8 + (row & 127);
       src = (const uint8_t*)(row < 128 ? a.w0 : a.w1);
     } else {
-      ch = it.ntile * kGemmDownChannels + row;
+      ch = it.ntile * kGemmDownChannelsFp8 + row;
       src = (const uint8_t*)a.w0;
     }
     ch = ch < N ? ch : N - 1;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ch = it.ntile * kGemmGateUpChannels + wm * 64 + i * 32 + q * 8 + lhi * 4;
+          const int ch = it.ntile * kGemmGateUpChannelsFp8 + wm * 64 + i * 32 + q * 8 + lhi * 4;
           const uint32_t pk = pack_fp8x4(hv[tj][i][q * 4 + 0] / s, hv[tj][i][q * 4 + 1] / s,
                                          hv[tj][i][q * 4 + 2] / s, hv[tj][i][q * 4 + 3] / s);
           *(uint32_t*)(h + ch) = pk;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ch = it.ntile * kGemmDownChannels + wm * 128 + t * 32 + q * 8 + lhi * 4;
+          const int ch = it.ntile * kGemmDownChannelsFp8 + wm * 128 + t * 32 + q * 8 + lhi * 4;
           if (ch >= N) continue;
           if (kOutF32) {
             f32x4 v = {acc[t][tj][q * 4 + 0], acc[t][tj][q * 4 + 1], acc[t][tj][q * 4 + 2],

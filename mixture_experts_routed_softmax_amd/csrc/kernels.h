@@ -71,9 +71,11 @@ struct GemmArgs {
 };
 
 // tile geometry of the grouped GEMMs
-constexpr int kGemmRowsPerTile = 128;   // token rows per tile
-constexpr int kGemmGateUpChannels = 128; // h channels per gate/up tile (256 weight rows)
-constexpr int kGemmDownChannels = 256;   // output channels per down tile
+constexpr int kGemmRowsPerTile = 128;          // token rows per tile (all dtypes)
+constexpr int kGemmGateUpChannelsBf16 = 256;   // h channels per bf16 gate/up tile (512 weight rows)
+constexpr int kGemmDownChannelsBf16 = 512;     // output channels per bf16 down tile
+constexpr int kGemmGateUpChannelsFp8 = 128;    // h channels per fp8 gate/up tile (256 weight rows)
+constexpr int kGemmDownChannelsFp8 = 256;      // output channels per fp8 down tile
 
 hipError_t launch_gate_up_bf16(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_down_bf16(const GemmArgs& a, int grid, hipStream_t stream);
