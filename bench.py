@@ -8,6 +8,10 @@ combine) over one batch of T synthetic tokens whose inputs and weights are
 already resident in HBM.  W untimed warmup steps are followed by exactly K
 timed steps, bracketed by torch.cuda.synchronize(); value = T * K / elapsed.
 
+Expert weights are packed into the tile-contiguous layout once before the
+timed steps (moe_pack_weights, a model-load transform; --layout rowmajor
+times the unpacked kernels instead).
+
 The default workload is the Qwen1.5-MoE-A2.7B-like prefill layer (T=4096,
 H=2048, I=1408, E=60, top-4 softmax without renormalisation, Zipf-skewed
 router bias, bf16).  Other workloads (--config) print the same line for
@@ -54,6 +58,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--layout", default="packed", choices=["packed", "rowmajor"],
+                   help="expert-weight layout; packed weights are written once before timing")
     return p.parse_args()
 
 
@@ -126,18 +132,26 @@ def main():
     torch.cuda.synchronize()
     log("inputs generated in %.1f s" % (time.perf_counter() - t0))
 
+    layout = args.layout if s.experts != "f32" else "rowmajor"
     d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,
                       routed_scale=s.routed_scale, act_dtype=s.act, w_dtype=s.experts,
-                      w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none")
+                      w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none", layout=layout)
+    if layout == "packed":
+        # one-time model-load transform, outside the timed region
+        wg, dn = moe.pack_experts(d, L["w_gate"], L["w_up"], L["w_down"], dev)
+        wu = None
+        del L["w_gate"], L["w_up"], L["w_down"]
+        torch.cuda.synchronize()
+    else:
+        wg, wu, dn = L["w_gate"], L["w_up"], L["w_down"]
     out = torch.empty(s.T, s.H, dtype=torch.float32 if s.act == "f32" else torch.bfloat16, device=dev)
     counts = torch.empty(s.E, dtype=torch.int32, device=dev)
     ws = moe.workspace(d, moe.MOE_OP_FORWARD, dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"],
-                        L["w_down"], L.get("s_gate"), L.get("s_up"), L.get("s_down"), out, None, None,
-                        counts, ws, stream)
+        moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], wg, wu, dn, L.get("s_gate"),
+                        L.get("s_up"), L.get("s_down"), out, None, None, counts, ws, stream)
 
     for _ in range(args.warmup):
         step()
@@ -208,7 +222,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        del ws
+        del ws, wg, wu, dn
+        L = synthetic.make_layer(s, seed=args.seed, device=dev)   # the same seeded inputs, row-major
         cpu = cpu_baseline(s, L, args.cpu_seconds)
         log("cpu baseline: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
 
@@ -219,7 +234,7 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[s.experts], "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
                    "experts": s.experts, "score": s.score, "renormalize": s.renormalize,
-                   "routed_scale": s.routed_scale, "router_bias": s.bias,
+                   "routed_scale": s.routed_scale, "router_bias": s.bias, "weights": layout,
                    **({"scale_fmt": s.scale_fmt} if s.experts == "fp8" else {}),
                    "layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1)},
         "roofline": roof,

@@ -77,6 +77,18 @@ typedef enum { MOE_ACT_NONE = 0, MOE_ACT_DYNAMIC = 1, MOE_ACT_STATIC = 2 } moe_a
  * different scheme); AUTO picks STREAM when T <= 64. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } moe_path;
 
+/* Layout of the expert weights passed to the expert GEMMs and moe_forward.
+ * ROWMAJOR: w_gate, w_up [E,I,H] and w_down [E,H,I] as described above.
+ * PACKED: the tile-contiguous layout written once by moe_pack_weights (a
+ * model-load transform): every (expert, 256-row tile, 64-byte K step) is one
+ * contiguous 16 KB chunk, so the GEMMs stream weights from HBM in long runs.
+ * With PACKED, w_gate is the packed gate/up buffer (gate and up rows of the
+ * same channels interleaved per tile), w_up is unused (pass NULL) and w_down
+ * is the packed down buffer.  Block scales keep their layout. */
+typedef enum { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
+
+typedef enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1 } moe_pack_which;
+
 typedef enum {
     MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GATE_UP = 2, MOE_OP_DOWN = 3,
     MOE_OP_COMBINE = 4, MOE_OP_FORWARD = 5
@@ -99,7 +111,8 @@ typedef struct moe_desc {
     int32_t act_scheme;    /* MOE_ACT_NONE, or MOE_ACT_DYNAMIC with FP8 weights */
     int32_t y_dtype;       /* expert-output rows y_sorted: MOE_DT_F32 or MOE_DT_BF16 */
     int32_t path;          /* moe_path */
-    int32_t reserved[3];   /* must be zero */
+    int32_t w_layout;      /* moe_layout of the expert weights */
+    int32_t reserved[2];   /* must be zero */
 } moe_desc;
 
 /* Supported combinations:
@@ -197,6 +210,22 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
                        const void* w_up_scales, const void* w_down_scales, void* out,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the packed copy of one weight set (MOE_PACK_GATE_UP: w_gate and
+ * w_up together; MOE_PACK_DOWN: w_down) for desc's shapes and weight dtype;
+ * 0 if the description is invalid or uses fp32 weights. */
+size_t moe_packed_weight_bytes(const moe_desc* desc, int which);
+
+/* Writes the packed layout of one weight set into dst (device, at least
+ * moe_packed_weight_bytes(desc, which) bytes, 256-byte aligned).
+ *   which = MOE_PACK_GATE_UP: w0 = w_gate, w1 = w_up (row-major [E,I,H])
+ *   which = MOE_PACK_DOWN:    w0 = w_down (row-major [E,H,I]), w1 = NULL
+ * Packed tile t of gate/up holds channels 128t .. 128t+127 (gate rows first,
+ * then the same channels of up); packed tile t of down holds output channels
+ * 256t .. 256t+255; rows past the end are zero.  desc->T and desc->w_layout
+ * are ignored.  bf16 and fp8 weights only. */
+moe_status moe_pack_weights(const moe_desc* desc, int which, const void* w0, const void* w1,
+                            void* dst, void* stream);
 
 /* Workspace bytes needed by `op` (a moe_op) for this description; 0 if the
  * op needs none or the description is invalid (the call itself then reports

@@ -33,6 +33,8 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 MOE_SCALE_NONE, MOE_SCALE_F32, MOE_SCALE_UE8M0 = range(3)
 MOE_ACT_NONE, MOE_ACT_DYNAMIC, MOE_ACT_STATIC = range(3)
 MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM = range(3)
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = range(2)
+MOE_PACK_GATE_UP, MOE_PACK_DOWN = range(2)
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GATE_UP, MOE_OP_DOWN, MOE_OP_COMBINE,
  MOE_OP_FORWARD) = range(6)
 STAGES = ("route", "hist", "scan", "scatter", "quant_x", "gate_up", "down", "combine")
@@ -46,7 +48,8 @@ class MoeDesc(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
                 ("w_scale_fmt", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("act_scheme", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
-                ("path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("path", ctypes.c_int32), ("w_layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class MoeError(RuntimeError):
@@ -71,6 +74,10 @@ _sigs = {
 for _name, _args in _sigs.items():
     getattr(_lib, _name).argtypes = _args
     getattr(_lib, _name).restype = ctypes.c_int
+_lib.moe_pack_weights.argtypes = [_DP, ctypes.c_int, _vp, _vp, _vp, _vp]
+_lib.moe_pack_weights.restype = ctypes.c_int
+_lib.moe_packed_weight_bytes.argtypes = [_DP, ctypes.c_int]
+_lib.moe_packed_weight_bytes.restype = ctypes.c_size_t
 _lib.moe_workspace_bytes.argtypes = [_DP, ctypes.c_int]
 _lib.moe_workspace_bytes.restype = ctypes.c_size_t
 _lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -95,7 +102,7 @@ def library():
 
 def make_desc(T, H, I, E, k, *, score="softmax", renormalize=False, routed_scale=1.0,
               act_dtype="bf16", w_dtype="bf16", w_scale_fmt="none", block=None,
-              act_scheme=None, y_dtype=None, path="auto") -> MoeDesc:
+              act_scheme=None, y_dtype=None, path="auto", layout="rowmajor") -> MoeDesc:
     dt = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "fp8": MOE_DT_FP8_E4M3}
     d = MoeDesc()
     d.T, d.H, d.I, d.E, d.k = int(T), int(H), int(I), int(E), int(k)
@@ -114,6 +121,7 @@ def make_desc(T, H, I, E, k, *, score="softmax", renormalize=False, routed_scale
         y_dtype = "f32" if act_dtype == "f32" else "bf16"
     d.y_dtype = dt[y_dtype]
     d.path = {"auto": MOE_PATH_AUTO, "grouped": MOE_PATH_GROUPED, "stream": MOE_PATH_STREAM}[path]
+    d.w_layout = {"rowmajor": MOE_LAYOUT_ROWMAJOR, "packed": MOE_LAYOUT_PACKED}[layout]
     return d
 
 
@@ -160,6 +168,25 @@ def workspace(desc: MoeDesc, op: int, device="cuda"):
 
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_packed_weight_bytes(desc: MoeDesc, which: int) -> int:
+    return int(_lib.moe_packed_weight_bytes(ctypes.byref(desc), int(which)))
+
+
+def moe_pack_weights(desc, which, w0, w1, dst, stream=None):
+    _check(_lib.moe_pack_weights(ctypes.byref(desc), int(which), _ptr(w0), _ptr(w1), _ptr(dst),
+                                 _stream(stream)))
+
+
+def pack_experts(desc, w_gate, w_up, w_down, device="cuda"):
+    """(packed gate/up, packed down) uint8 device tensors for desc's shapes."""
+    import torch
+    gu = torch.empty(moe_packed_weight_bytes(desc, MOE_PACK_GATE_UP), dtype=torch.uint8, device=device)
+    dn = torch.empty(moe_packed_weight_bytes(desc, MOE_PACK_DOWN), dtype=torch.uint8, device=device)
+    moe_pack_weights(desc, MOE_PACK_GATE_UP, w_gate, w_up, gu)
+    moe_pack_weights(desc, MOE_PACK_DOWN, w_down, None, dn)
+    return gu, dn
 
 
 def moe_route_topk(desc, x, w_router, router_bias, topk_ids, topk_w, stream=None):

@@ -69,6 +69,10 @@ moe_status validate(const moe_desc* d) {
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_STREAM) return fail(MOE_EINVAL, "path = %d", d->path);
   for (int r : d->reserved)
     if (r != 0) return fail(MOE_EINVAL, "reserved fields must be zero");
+  if (d->w_layout != MOE_LAYOUT_ROWMAJOR && d->w_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_EINVAL, "w_layout = %d", d->w_layout);
+  if (d->w_layout == MOE_LAYOUT_PACKED && d->w_dtype == MOE_DT_F32)
+    return fail(MOE_EUNSUPPORTED, "packed weights are bf16 or fp8");
   if (d->T * (int64_t)d->k > (int64_t)INT32_MAX / 2)
     return fail(MOE_EUNSUPPORTED, "T*k = %lld too large", (long long)(d->T * d->k));
   if (d->w_scale_fmt < MOE_SCALE_NONE || d->w_scale_fmt > MOE_SCALE_UE8M0)
@@ -117,18 +121,37 @@ struct Carve {
   }
 };
 
+bool packed(const moe_desc* d) { return d->w_layout == MOE_LAYOUT_PACKED; }
+
 int gate_up_ntiles(const moe_desc* d) {
-  const int c = d->w_dtype == MOE_DT_FP8_E4M3 ? kGemmGateUpChannelsFp8 : kGemmGateUpChannelsBf16;
+  const int c = packed(d) ? kPackedGateUpChannels
+                          : (d->w_dtype == MOE_DT_FP8_E4M3 ? kGemmGateUpChannelsFp8 : kGemmGateUpChannelsBf16);
   return (d->I + c - 1) / c;
 }
 int down_ntiles(const moe_desc* d) {
-  const int c = d->w_dtype == MOE_DT_FP8_E4M3 ? kGemmDownChannelsFp8 : kGemmDownChannelsBf16;
+  const int c = packed(d) ? kPackedDownChannels
+                          : (d->w_dtype == MOE_DT_FP8_E4M3 ? kGemmDownChannelsFp8 : kGemmDownChannelsBf16);
   return (d->H + c - 1) / c;
+}
+
+size_t packed_bytes(const moe_desc* d, int which) {
+  const int gate_up = which == MOE_PACK_GATE_UP;
+  const int64_t N = gate_up ? d->I : d->H;
+  const int64_t K = gate_up ? d->H : d->I;
+  const int64_t tiles = packed_tiles(gate_up, (int)N);
+  return (size_t)d->E * tiles * 256 * K * elt_bytes(d->w_dtype);
+}
+
+// token rows per grouped-GEMM tile
+int rows_per_tile(const moe_desc* d) {
+  if (packed(d)) return is_fp8(d) ? kPackedTokFp8 : kPackedTokBf16;
+  return kGemmRowsPerTile;
 }
 
 int64_t sched_capacity(const moe_desc* d, int ntiles) {
   const int64_t P = pairs(d);
-  const int64_t tiles = (P + kGemmRowsPerTile - 1) / kGemmRowsPerTile + std::min<int64_t>(d->E, P);
+  const int bm = rows_per_tile(d);
+  const int64_t tiles = (P + bm - 1) / bm + std::min<int64_t>(d->E, P);
   return tiles * ntiles;
 }
 
@@ -264,7 +287,7 @@ struct StageTimer {
 SchedRequest sched_req(Schedule* s, const moe_desc* d, int ntiles) {
   SchedRequest r{};
   r.sched = s;
-  r.rows_per_tile = kGemmRowsPerTile;
+  r.rows_per_tile = rows_per_tile(d);
   r.ntiles = ntiles;
   r.capacity = (int)sched_capacity(d, ntiles);
   return r;
@@ -318,10 +341,12 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   a.out_f32 = d->w_dtype == MOE_DT_F32;
   a.sched = sched;
   a.offsets = offsets;
+  a.wtiles = (int)packed_tiles(1, d->I);
   StageTimer tm(MOE_STAGE_GATE_UP, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
-  if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
+  if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 0, grid, st);
+  else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
   else e = launch_gate_up_fp8(a, grid, st);
   MOE_TRY_HIP(e, "gate/up launch");
@@ -341,10 +366,12 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   a.out_f32 = d->y_dtype == MOE_DT_F32;
   a.sched = sched;
   a.offsets = offsets;
+  a.wtiles = (int)packed_tiles(0, d->H);
   StageTimer tm(MOE_STAGE_DOWN, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
-  if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
+  if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 1, grid, st);
+  else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);
   else e = launch_down_fp8(a, grid, st);
   MOE_TRY_HIP(e, "down launch");
@@ -434,10 +461,10 @@ moe_status moe_expert_gate_up_swiglu(const moe_desc* d, const void* x_sorted, co
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (pairs(d) == 0) return MOE_OK;
-  if (!x_sorted || !offsets || !w_gate || !w_up || !h) return fail(MOE_EINVAL, "NULL tensor argument");
+  if (!x_sorted || !offsets || !w_gate || (!w_up && !packed(d)) || !h) return fail(MOE_EINVAL, "NULL tensor argument");
   if (is_fp8(d) && (!x_scales || !w_gate_scales || !w_up_scales || !h_scales))
     return fail(MOE_EINVAL, "fp8 experts need x_scales, weight scales and h_scales");
-  if (!aligned16(x_sorted) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h))
+  if (!aligned16(x_sorted) || !aligned16(w_gate) || (!packed(d) && !aligned16(w_up)) || !aligned16(h))
     return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
   if ((s = check_ws(d, MOE_OP_GATE_UP, ws, ws_bytes)) != MOE_OK) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -496,10 +523,11 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
   if (s != MOE_OK) return s;
   if ((s = check_ws(d, MOE_OP_FORWARD, ws, ws_bytes)) != MOE_OK) return s;
   if (d->T > 0) {
-    if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return fail(MOE_EINVAL, "NULL tensor argument");
+    if (!x || !w_router || !w_gate || (!w_up && !packed(d)) || !w_down || !out)
+      return fail(MOE_EINVAL, "NULL tensor argument");
     if (is_fp8(d) && (!sg || !su || !sd)) return fail(MOE_EINVAL, "fp8 experts need all three block-scale tensors");
-    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-        !aligned16(out))
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || (!packed(d) && !aligned16(w_up)) ||
+        !aligned16(w_down) || !aligned16(out))
       return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
   }
   hipStream_t st = (hipStream_t)stream;
@@ -542,6 +570,29 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
                                d->act_dtype == MOE_DT_F32, st),
                 "combine launch");
   }
+  return MOE_OK;
+}
+
+size_t moe_packed_weight_bytes(const moe_desc* d, int which) {
+  if (validate(d) != MOE_OK || d->w_dtype == MOE_DT_F32) return 0;
+  if (which != MOE_PACK_GATE_UP && which != MOE_PACK_DOWN) return 0;
+  return packed_bytes(d, which);
+}
+
+moe_status moe_pack_weights(const moe_desc* d, int which, const void* w0, const void* w1, void* dst,
+                            void* stream) {
+  g_err.clear();
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (d->w_dtype == MOE_DT_F32) return fail(MOE_EUNSUPPORTED, "packed weights are bf16 or fp8");
+  if (which != MOE_PACK_GATE_UP && which != MOE_PACK_DOWN) return fail(MOE_EINVAL, "which = %d", which);
+  const int gate_up = which == MOE_PACK_GATE_UP;
+  if (!w0 || !dst || (gate_up && !w1)) return fail(MOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(w0) || (gate_up && !aligned16(w1)) || ((uintptr_t)dst & (kAlign - 1)))
+    return fail(MOE_EINVAL, "weights must be 16-byte and dst 256-byte aligned");
+  const int N = gate_up ? d->I : d->H;
+  const int64_t row_bytes = (int64_t)(gate_up ? d->H : d->I) * elt_bytes(d->w_dtype);
+  MOE_TRY_HIP(launch_pack(w0, w1, gate_up, d->E, N, row_bytes, dst, (hipStream_t)stream), "pack launch");
   return MOE_OK;
 }
 

@@ -68,6 +68,7 @@ struct GemmArgs {
   const int32_t* offsets;   // f32 path: expert of a row
   int E;
   int64_t P;
+  int wtiles;               // packed weights: row tiles per expert
 };
 
 // tile geometry of the grouped GEMMs
@@ -82,6 +83,17 @@ hipError_t launch_down_bf16(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_gate_up_fp8(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_down_fp8(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t stream);
+// grouped GEMM on tile-packed weights (bf16 or fp8), mode 0 gate/up, 1 down
+hipError_t launch_gemm_packed(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream);
+constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
+constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
+constexpr int kPackedTokBf16 = 256;          // token rows per packed bf16 tile
+constexpr int kPackedTokFp8 = 128;           // token rows per packed fp8 tile
+
+// ---- weight packing (one-time layout transform)
+int64_t packed_tiles(int which_gate_up, int N);
+hipError_t launch_pack(const void* w0, const void* w1, int gate_up, int E, int N, int64_t row_bytes,
+                       void* dst, hipStream_t stream);
 hipError_t launch_down_f32(const GemmArgs& a, hipStream_t stream);
 
 // ---- combine

@@ -20,12 +20,21 @@ def tol_of(s: synthetic.LayerSpec) -> float:
     return TOL[s.experts]
 
 
-def desc_for(s: synthetic.LayerSpec, T: int | None = None, path: str = "auto", y_dtype=None):
+def desc_for(s: synthetic.LayerSpec, T: int | None = None, path: str = "auto", y_dtype=None,
+             layout: str = "rowmajor"):
     return moe.make_desc(s.T if T is None else T, s.H, s.I, s.E, s.k, score=s.score,
                          renormalize=s.renormalize, routed_scale=s.routed_scale,
                          act_dtype=s.act, w_dtype=s.experts,
                          w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none",
-                         y_dtype=y_dtype, path=path)
+                         y_dtype=y_dtype, path=path, layout=layout)
+
+
+def expert_weights(d, L: dict):
+    """(w_gate, w_up, w_down) as the GEMMs take them for d's layout."""
+    if d.w_layout == moe.MOE_LAYOUT_PACKED:
+        gu, dn = moe.pack_experts(d, L["w_gate"], L["w_up"], L["w_down"], L["x"].device)
+        return gu, None, dn
+    return L["w_gate"], L["w_up"], L["w_down"]
 
 
 def score_code(s):
@@ -101,27 +110,28 @@ def dequant_rows(codes: torch.Tensor, scales: torch.Tensor, group: int = 128) ->
     return v * np.repeat(s, group, axis=1)
 
 
-def run_forward(s, L: dict, T=None, path="auto", y_dtype=None):
+def run_forward(s, L: dict, T=None, path="auto", y_dtype=None, layout="rowmajor"):
     """moe_forward on device tensors L; returns (out, ids, w, counts)."""
     T = s.T if T is None else T
-    d = desc_for(s, T, path, y_dtype)
+    d = desc_for(s, T, path, y_dtype, layout)
+    wg, wu, wd = expert_weights(d, L)
     dev = L["x"].device
     out = torch.empty(T, s.H, dtype=act_dtype(s), device=dev)
     ids = torch.empty(T, s.k, dtype=torch.int32, device=dev)
     w = torch.empty(T, s.k, dtype=torch.float32, device=dev)
     counts = torch.empty(s.E, dtype=torch.int32, device=dev)
     ws = moe.workspace(d, moe.MOE_OP_FORWARD, dev)
-    moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"],
-                    L["w_down"], L.get("s_gate"), L.get("s_up"), L.get("s_down"), out, ids, w,
-                    counts, ws)
+    moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], wg, wu, wd, L.get("s_gate"),
+                    L.get("s_up"), L.get("s_down"), out, ids, w, counts, ws)
     torch.cuda.synchronize()
     return out, ids, w, counts
 
 
-def run_staged(s, L: dict, ids_in: torch.Tensor, w_in: torch.Tensor, y_dtype=None):
+def run_staged(s, L: dict, ids_in: torch.Tensor, w_in: torch.Tensor, y_dtype=None, layout="rowmajor"):
     """The five staged entry points on given routing; returns a dict of results."""
     T = ids_in.shape[0]
-    d = desc_for(s, T, "grouped", y_dtype)
+    d = desc_for(s, T, "grouped", y_dtype, layout)
+    wg, wu, wd = expert_weights(d, L)
     dev = L["x"].device
     P = T * s.k
     fp8 = s.experts == "fp8"
@@ -146,14 +156,12 @@ def run_staged(s, L: dict, ids_in: torch.Tensor, w_in: torch.Tensor, y_dtype=Non
         r["h"] = torch.empty(P, s.I, dtype=act_dtype(s), device=dev)
         r["h_scales"] = None
     ws = moe.workspace(d, moe.MOE_OP_GATE_UP, dev)
-    moe.moe_expert_gate_up_swiglu(d, r["x_sorted"], r["x_scales"], r["offsets"], L["w_gate"],
-                                  L["w_up"], L.get("s_gate"), L.get("s_up"), r["h"], r["h_scales"],
-                                  ws)
+    moe.moe_expert_gate_up_swiglu(d, r["x_sorted"], r["x_scales"], r["offsets"], wg, wu,
+                                  L.get("s_gate"), L.get("s_up"), r["h"], r["h_scales"], ws)
     ydt = torch.float32 if d.y_dtype == moe.MOE_DT_F32 else torch.bfloat16
     r["y"] = torch.empty(P, s.H, dtype=ydt, device=dev)
     ws = moe.workspace(d, moe.MOE_OP_DOWN, dev)
-    moe.moe_expert_down(d, r["h"], r["h_scales"], r["offsets"], L["w_down"], L.get("s_down"),
-                        r["y"], ws)
+    moe.moe_expert_down(d, r["h"], r["h_scales"], r["offsets"], wd, L.get("s_down"), r["y"], ws)
     r["out"] = torch.empty(T, s.H, dtype=act_dtype(s), device=dev)
     moe.moe_unpermute_combine(d, r["y"], r["inv"], w_in, r["out"])
     torch.cuda.synchronize()

@@ -1,5 +1,5 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-times (moe_forward, default path).
+times (moe_forward, default path, packed expert weights).
 
 Routing and the permutation are checked for all tokens, bit for bit, against
 the oracle.  The expert outputs are checked on a coverage sample the oracle
@@ -20,9 +20,9 @@ from moe_cases import (coverage_tokens, host, oracle_experts, oracle_route, row_
 pytestmark = pytest.mark.gpu
 
 
-def _full_case(s, seed, n_random, limit):
+def _full_case(s, seed, n_random, limit, layout="packed"):
     L = synthetic.make_layer(s, seed=seed, device="cuda")
-    out, ids, w, counts = run_forward(s, L)
+    out, ids, w, counts = run_forward(s, L, layout=layout)
     hl = host(L)
     del L
     gc.collect()

@@ -31,10 +31,15 @@ def _layer(s, seed=0):
     return L, host(L)
 
 
-def _check_forward(s, L, hl, seed=0, y_dtype=None):
+LAYOUTS = {name: (["rowmajor"] if s.experts == "f32" else ["rowmajor", "packed"])
+           for name, s in SMALL.items()}
+CASES = [(n, lay) for n in SMALL for lay in LAYOUTS[n]]
+
+
+def _check_forward(s, L, hl, seed=0, y_dtype=None, layout="rowmajor"):
     ids_o, w_o = oracle_route(s, hl)
     counts_o, offsets_o, perm_o, inv_o = oracle.permute(ids_o, s.E)
-    out, ids, w, counts = run_forward(s, L, y_dtype=y_dtype)
+    out, ids, w, counts = run_forward(s, L, y_dtype=y_dtype, layout=layout)
     assert np.array_equal(ids.cpu().numpy(), ids_o), "router ids differ from the oracle"
     assert np.array_equal(counts.cpu().numpy(), counts_o)
     np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=1e-5, atol=1e-7)
@@ -46,15 +51,15 @@ def _check_forward(s, L, hl, seed=0, y_dtype=None):
     return out
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_forward_small(name):
+@pytest.mark.parametrize("name,layout", CASES)
+def test_forward_small(name, layout):
     s = SMALL[name]
     L, hl = _layer(s)
-    _check_forward(s, L, hl)
+    _check_forward(s, L, hl, layout=layout)
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_staged_small(name):
+@pytest.mark.parametrize("name,layout", CASES)
+def test_staged_small(name, layout):
     s = SMALL[name]
     L, hl = _layer(s, seed=1)
     ids_o, w_o = oracle_route(s, hl)
@@ -68,7 +73,7 @@ def test_staged_small(name):
     # the rest of the chain on the oracle's routing
     ids_in = torch.from_numpy(ids_o).cuda()
     w_in = torch.from_numpy(w_o.astype(np.float32)).cuda()
-    r = run_staged(s, L, ids_in, w_in)
+    r = run_staged(s, L, ids_in, w_in, layout=layout)
     counts_o, offsets_o, perm_o, inv_o = oracle.permute(ids_o, s.E)
     assert np.array_equal(r["counts"].cpu().numpy(), counts_o)
     assert np.array_equal(r["offsets"].cpu().numpy(), offsets_o)
@@ -108,10 +113,48 @@ def test_forward_deterministic():
     assert torch.equal(a, b)
 
 
-def test_forward_f32_intermediate_rows():
+@pytest.mark.parametrize("layout", ["rowmajor", "packed"])
+def test_forward_f32_intermediate_rows(layout):
     s = SMALL["bf16_sigmoid"]
     L, hl = _layer(s, seed=4)
-    _check_forward(s, L, hl, y_dtype="f32")
+    _check_forward(s, L, hl, y_dtype="f32", layout=layout)
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "fp8_f32"])
+def test_packed_layout_bytes(name):
+    """moe_pack_weights writes the layout include/moe.h documents (checked
+    against a numpy construction of that description)."""
+    s = SMALL[name]
+    L = synthetic.make_layer(s, seed=2, device="cuda")
+    d = desc_for(s, layout="packed")
+    gu, dn = moe.pack_experts(d, L["w_gate"], L["w_up"], L["w_down"])
+    torch.cuda.synchronize()
+
+    def raw(t):
+        t = t.cpu().contiguous()
+        return t.view(torch.uint8).numpy().reshape(t.shape[0], t.shape[1], -1)
+
+    def expect(mats, rows_per_tile):
+        E, N, RB = mats[0].shape
+        NT = -(-N // (rows_per_tile // len(mats)))
+        KT = RB // 64
+        out = np.zeros((E, NT, KT, 256, 4, 16), np.uint8)
+        rows = np.arange(256)
+        for nt in range(NT):
+            for m, W in enumerate(mats):
+                per = 256 // len(mats)
+                n = nt * per + np.arange(per)
+                ok = n < N
+                for kt in range(KT):
+                    for p in range(4):
+                        r = m * per + np.arange(per)
+                        c = p ^ ((r >> 2) & 3)
+                        for i in np.nonzero(ok)[0]:
+                            out[:, nt, kt, r[i], p, :] = W[:, n[i], kt * 64 + c[i] * 16: kt * 64 + c[i] * 16 + 16]
+        return out.reshape(-1)
+
+    assert np.array_equal(gu.cpu().numpy(), expect([raw(L["w_gate"]), raw(L["w_up"])], 256))
+    assert np.array_equal(dn.cpu().numpy(), expect([raw(L["w_down"])], 256))
 
 
 # ------------------------------------------------------------------ edge cases
