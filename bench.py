@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (to scale rocprofv3 byte counters) and exit")
     p.add_argument("--layout", default="packed", choices=["packed", "rowmajor"],
                    help="expert-weight layout; packed weights are written once before timing")
     return p.parse_args()
@@ -65,6 +67,24 @@ def parse():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from its committed rocprofv3 counter
+    record (profiles/*.<workload>.traffic.json, FETCH_SIZE and WRITE_SIZE scaled
+    by a plain-copy calibration), or None if there is none or the kernel's
+    source changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.%s.traffic.json" % workload)):
+        rec = json.load(open(path))
+        if rec.get("kernel") != kernel:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(s, L, budget_s: float):
@@ -120,6 +140,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a plain copy kernel of known size: it reads and writes exactly 1 GiB
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of %d bytes" % src.numel())
+        return
     over = {}
     if args.T is not None:
         over["T"] = args.T
@@ -210,8 +239,11 @@ def main():
         flops = 2.0 * P * s.H * 2 * s.I
         achieved = flops / (avg_ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[s.experts]
+        kname = "gemm_packed_kernel<%s, 0, false>" % ("true" if s.experts == "fp8" else "false")
+        traffic = recorded_traffic(s.name, kname) if layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "kernel": "gate_up grouped GEMM (%s)" % s.experts,
                 "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": flops}
     layer_flops = 2.0 * P * 3 * s.H * s.I
