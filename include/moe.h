@@ -70,11 +70,12 @@ typedef enum { MOE_SCALE_NONE = 0, MOE_SCALE_F32 = 1, MOE_SCALE_UE8M0 = 2 } moe_
  * per-row scales are required, static per-tensor scales are rejected). */
 typedef enum { MOE_ACT_NONE = 0, MOE_ACT_DYNAMIC = 1, MOE_ACT_STATIC = 2 } moe_act_scheme;
 
-/* Expert-GEMM strategy of moe_forward.  GROUPED runs tiled grouped GEMMs over
- * the expert-sorted rows; STREAM reads every touched expert's weights exactly
- * once, split over all compute units (for decode-sized batches, T <= 64; the
- * section "Decode-stage switching" notes that small token counts want a
- * different scheme); AUTO picks STREAM when T <= 64. */
+/* Expert-GEMM strategy (moe_forward and the two expert-GEMM calls).  GROUPED
+ * runs tiled grouped GEMMs over the expert-sorted rows; STREAM reads every
+ * touched expert's weights exactly once, split over all compute units, for
+ * decode-sized batches (section "Decode-stage switching": small token counts
+ * want a different scheme); it needs packed weights and T <= 64 (else
+ * MOE_EUNSUPPORTED).  AUTO picks STREAM for packed weights with T <= 64. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } moe_path;
 
 /* Layout of the expert weights passed to the expert GEMMs and moe_forward.
@@ -136,10 +137,12 @@ typedef struct moe_desc {
  *   topk_w      [T,k] fp32 out: score of each selected expert (softmax over
  *               all E, or sigmoid), divided by the sum of the k selected scores
  *               if desc->renormalize, times desc->routed_scale
- * Logits accumulate in fp32. */
+ *   ws, ws_bytes  workspace of moe_workspace_bytes(desc, MOE_OP_ROUTE) (bf16:
+ *               partial logits of the K slices; fp32 needs none)
+ * Logits accumulate in fp32; the K slices are added in a fixed order. */
 moe_status moe_route_topk(const moe_desc* desc, const void* x, const void* w_router,
                           const float* router_bias, int32_t* topk_ids, float* topk_w,
-                          void* stream);
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Order (token, slot) pairs by expert (backend table, rows grouped_mm and
  * deepgemm: tokens are ordered / sorted by selected expert).

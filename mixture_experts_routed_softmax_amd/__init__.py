@@ -62,7 +62,7 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _DP = ctypes.POINTER(MoeDesc)
 _sigs = {
-    "moe_route_topk": [_DP, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_route_topk": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
     "moe_permute": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
     "moe_expert_gate_up_swiglu": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp],
@@ -189,9 +189,9 @@ def pack_experts(desc, w_gate, w_up, w_down, device="cuda"):
     return gu, dn
 
 
-def moe_route_topk(desc, x, w_router, router_bias, topk_ids, topk_w, stream=None):
+def moe_route_topk(desc, x, w_router, router_bias, topk_ids, topk_w, ws=None, stream=None):
     _check(_lib.moe_route_topk(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                               _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+                               _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_permute(desc, topk_ids, x, counts, offsets, perm, inv, x_sorted=None, x_sorted_scales=None,

@@ -103,8 +103,8 @@ moe_status validate(const moe_desc* d) {
     if (d->w_dtype == MOE_DT_F32 && (d->H % 8 || d->I % 8))
       return fail(MOE_EUNSUPPORTED, "fp32 experts need H and I multiples of 8");
   }
-  if (d->path == MOE_PATH_STREAM)
-    return fail(MOE_EUNSUPPORTED, "the weight-streaming path is not available in this build");
+  if (d->path == MOE_PATH_STREAM && (d->w_layout != MOE_LAYOUT_PACKED || d->T > kStreamMaxTokens))
+    return fail(MOE_EUNSUPPORTED, "the weight-streaming path needs packed weights and T <= %d", kStreamMaxTokens);
   return MOE_OK;
 }
 
@@ -142,8 +142,14 @@ size_t packed_bytes(const moe_desc* d, int which) {
   return (size_t)d->E * tiles * 256 * K * elt_bytes(d->w_dtype);
 }
 
+// expert GEMMs stream the touched experts' weights (decode-sized batches)
+bool use_stream(const moe_desc* d) {
+  return packed(d) && d->T <= kStreamMaxTokens && (d->path == MOE_PATH_STREAM || d->path == MOE_PATH_AUTO);
+}
+
 // token rows per grouped-GEMM tile
 int rows_per_tile(const moe_desc* d) {
+  if (use_stream(d)) return kStreamMaxTokens;
   if (packed(d)) return is_fp8(d) ? kPackedTokFp8 : kPackedTokBf16;
   return kGemmRowsPerTile;
 }
@@ -183,6 +189,7 @@ PermuteWs carve_permute(Carve& c, const moe_desc* d, bool with_quant) {
 }
 
 struct ForwardWs {
+  float* route_part;
   int32_t* ids;
   float* w;
   int32_t* counts;
@@ -201,6 +208,7 @@ struct ForwardWs {
 ForwardWs carve_forward(Carve& c, const moe_desc* d) {
   const int64_t P = pairs(d);
   ForwardWs w{};
+  w.route_part = (float*)c.take<uint8_t>(route_workspace_bytes(d->T, d->H, d->E, d->act_dtype == MOE_DT_BF16));
   w.ids = c.take<int32_t>(P);
   w.w = c.take<float>(P);
   w.counts = c.take<int32_t>(d->E);
@@ -222,7 +230,7 @@ ForwardWs carve_forward(Carve& c, const moe_desc* d) {
 size_t ws_size(const moe_desc* d, int op) {
   Carve c{nullptr};
   switch (op) {
-    case MOE_OP_ROUTE: return 0;
+    case MOE_OP_ROUTE: return align_up(route_workspace_bytes(d->T, d->H, d->E, d->act_dtype == MOE_DT_BF16));
     case MOE_OP_PERMUTE: carve_permute(c, d, is_fp8(d)); return c.off;
     case MOE_OP_GATE_UP:
       return d->w_dtype == MOE_DT_F32 ? 0 : align_up(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
@@ -345,7 +353,8 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   StageTimer tm(MOE_STAGE_GATE_UP, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
-  if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 0, grid, st);
+  if (use_stream(d)) e = launch_gemm_stream(a, is_fp8(d), 0, grid, st);
+  else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
   else e = launch_gate_up_fp8(a, grid, st);
@@ -370,7 +379,8 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   StageTimer tm(MOE_STAGE_DOWN, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
-  if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 1, grid, st);
+  if (use_stream(d)) e = launch_gemm_stream(a, is_fp8(d), 1, grid, st);
+  else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);
   else e = launch_down_fp8(a, grid, st);
@@ -402,17 +412,18 @@ size_t moe_workspace_bytes(const moe_desc* d, int op) {
 }
 
 moe_status moe_route_topk(const moe_desc* d, const void* x, const void* w_router, const float* bias,
-                          int32_t* ids, float* w, void* stream) {
+                          int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (d->T == 0) return MOE_OK;
   if (!x || !w_router || !ids || !w) return fail(MOE_EINVAL, "NULL tensor argument");
   if (!aligned16(x) || !aligned16(w_router)) return fail(MOE_EINVAL, "x and w_router must be 16-byte aligned");
+  if ((s = check_ws(d, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   StageTimer tm(MOE_STAGE_ROUTE, st);
   MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, d->H, d->E, d->k, d->act_dtype == MOE_DT_BF16,
-                                d->score, d->renormalize, d->routed_scale, ids, w, st),
+                                d->score, d->renormalize, d->routed_scale, ids, w, (float*)ws, st),
               "router launch");
   return MOE_OK;
 }
@@ -541,7 +552,7 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
   if (d->T > 0) {
     StageTimer tm(MOE_STAGE_ROUTE, st);
     MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, d->H, d->E, d->k, d->act_dtype == MOE_DT_BF16,
-                                  d->score, d->renormalize, d->routed_scale, ids, w, st),
+                                  d->score, d->renormalize, d->routed_scale, ids, w, fw.route_part, st),
                 "router launch");
   }
   SchedRequest sgu{}, sdn{};

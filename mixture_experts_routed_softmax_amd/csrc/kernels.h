@@ -9,9 +9,12 @@ struct WorkItem;
 struct Schedule;
 
 // ---- router
+// bf16: `part` is a workspace of route_workspace_bytes() for the partial logits
 hipError_t launch_route_topk(const void* x, const void* w_router, const float* bias, int64_t T,
                              int H, int E, int k, int act_bf16, int score, int renorm,
-                             float routed_scale, int32_t* ids, float* w, hipStream_t stream);
+                             float routed_scale, int32_t* ids, float* w, float* part, hipStream_t stream);
+int route_slices(int64_t T, int H, int E);
+size_t route_workspace_bytes(int64_t T, int H, int E, int act_bf16);
 
 // ---- permutation
 constexpr int kPermChunk = 1024;   // (token, slot) pairs per histogram / scatter block
@@ -87,6 +90,9 @@ hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_packed(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
 constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
+// weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per touched expert)
+hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream);
+constexpr int kStreamMaxTokens = 64;
 constexpr int kPackedTokBf16 = 256;          // token rows per packed bf16 tile
 constexpr int kPackedTokFp8 = 128;           // token rows per packed fp8 tile
 

@@ -127,10 +127,11 @@ def run_forward(s, L: dict, T=None, path="auto", y_dtype=None, layout="rowmajor"
     return out, ids, w, counts
 
 
-def run_staged(s, L: dict, ids_in: torch.Tensor, w_in: torch.Tensor, y_dtype=None, layout="rowmajor"):
+def run_staged(s, L: dict, ids_in: torch.Tensor, w_in: torch.Tensor, y_dtype=None, layout="rowmajor",
+               path="grouped"):
     """The five staged entry points on given routing; returns a dict of results."""
     T = ids_in.shape[0]
-    d = desc_for(s, T, "grouped", y_dtype, layout)
+    d = desc_for(s, T, path, y_dtype, layout)
     wg, wu, wd = expert_weights(d, L)
     dev = L["x"].device
     P = T * s.k

@@ -120,7 +120,7 @@ def test_workspace_required_and_sized():
     P = 4096 * 4
     assert need >= P * 1408 * 2 + P * 2048 * 2
     assert _status_of(_forward_nulls, d) == moe.MOE_EWORKSPACE
-    assert moe.moe_workspace_bytes(d, moe.MOE_OP_ROUTE) == 0
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_ROUTE) > 0     # bf16 router: partial logits
     assert moe.moe_workspace_bytes(d, moe.MOE_OP_PERMUTE) > 0
     assert moe.moe_workspace_bytes(d, moe.MOE_OP_GATE_UP) > 0
     assert moe.moe_workspace_bytes(d, moe.MOE_OP_DOWN) > 0
@@ -133,16 +133,17 @@ def test_workspace_required_and_sized():
 def test_null_tensors_rejected_before_launch():
     d = moe.make_desc(16, 2048, 1408, 60, 4)
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_route_topk(d, None, None, None, None, None, stream=0)
+        moe.moe_route_topk(d, None, None, None, None, None, None, stream=0)
     assert ei.value.status == moe.MOE_EINVAL
 
 
 def test_empty_route_is_noop():
     d = moe.make_desc(0, 2048, 1408, 60, 4)
-    moe.moe_route_topk(d, None, None, None, None, None, stream=0)
+    moe.moe_route_topk(d, None, None, None, None, None, None, stream=0)
 
 
-def test_stream_path_reported_unsupported_until_built():
-    d = _qwen(path="stream")
-    st = _status_of(_forward_nulls, d)
-    assert st in (moe.MOE_EUNSUPPORTED, moe.MOE_EWORKSPACE)
+def test_stream_path_needs_packed_weights_and_small_batches():
+    assert _status_of(_forward_nulls, _qwen(path="stream", layout="packed")) == moe.MOE_EUNSUPPORTED  # T=4096
+    assert _status_of(_forward_nulls, moe.make_desc(64, 2048, 1408, 60, 4, path="stream")) == moe.MOE_EUNSUPPORTED
+    d = moe.make_desc(64, 2048, 1408, 60, 4, path="stream", layout="packed")
+    assert _status_of(_forward_nulls, d) == moe.MOE_EWORKSPACE   # valid request, no workspace given
