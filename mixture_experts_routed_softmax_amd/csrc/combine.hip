@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       i32x4 pk;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        pk[q] = (int)(f32_to_bf16_bits(acc[2 * q]) | ((uint32_t)f32_to_bf16_bits(acc[2 * q + 1]) << 16));
+        pk[q] = (int)pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
       *(i32x4*)((uint16_t*)out + o) = pk;
     }
   }

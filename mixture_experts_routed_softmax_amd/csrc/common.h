@@ -37,14 +37,20 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 }
 
 // round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN)
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// two fp32 -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
+
+// silu(g) = g * sigmoid(g); v_rcp_f32 (1 ulp) instead of an IEEE division
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // value of an E8M0 scale byte: 2^(b-127)
 __device__ __forceinline__ float e8m0_to_f32(uint8_t b) { return __builtin_ldexpf(1.0f, (int)b - 127); }

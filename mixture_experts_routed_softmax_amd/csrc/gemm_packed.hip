@@ -77,6 +77,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(n): at most n LDS reads of this wave still in flight
+template <int n>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(n >= 0 && n < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (n << 8));
+}
+
 template <int kLoads>
 __device__ __forceinline__ void wait_steps(int ahead) {
   switch (ahead) {
@@ -136,13 +143,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     const int c = (lane & 3) ^ ((row >> 2) & 3);
     bsrc[i] = (const uint8_t*)a.act + src_row * (int64_t)K * elt + c * 16;
   }
+  // wave-uniform parts of the DMA addresses (M0 takes the LDS address)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* asrc = abase + lane * 16 + wv * 1024;
   auto issue = [&](int stage, int kt) {
-    uint8_t* sb = smem + stage * kStage;
-    const uint8_t* src = abase + (int64_t)kt * kA + lane * 16;
+    uint8_t* sb = smem + stage * kStage + wv * 1024;
+    const uint8_t* src = asrc + (int64_t)kt * kA;
+    lds_load16(src, sb);
+    lds_load16(src + 8192, sb + 8192);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_load16(src + (i * 8 + wave) * 1024, sb + (i * 8 + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < kBI; ++i) lds_load16(bsrc[i] + (int64_t)kt * kRowB, sb + kA + (i * 8 + wave) * 1024);
+    for (int i = 0; i < kBI; ++i) lds_load16(bsrc[i] + (int64_t)kt * kRowB, sb + kA + i * 8192);
   };
 
   // LDS rows of this wave's tiles
@@ -157,33 +167,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
   const int brow = tg * kNTW * 32;
 
   typedef Frag<kFp8> F;
-  auto read = [&](int stage, F& f, auto nt_const) {
-    constexpr int NT = decltype(nt_const)::value;
+  // The fragments of a K step are consumed in two halves (bf16: the two
+  // 16-deep MFMA K slices; fp8: token tile 0, then the weight tiles with the
+  // other token tiles).  A half is refilled from the next step's stage as
+  // soon as its MFMAs are issued, so the LDS reads of step s+1 overlap the
+  // MFMAs of step s without a second register set.
+  auto read_half = [&](int stage, F& f, auto h_const, auto nt_const) {
+    constexpr int NT = decltype(nt_const)::value, h = decltype(h_const)::value;
     const uint8_t* sa = smem + stage * kStage;
     const uint8_t* sb = sa + kA;
     if constexpr (kFp8) {
+      auto ld8 = [&](const uint8_t* base, int row) {
+        i32x4 lo = *(const i32x4*)(base + swz(row, hl * 2));
+        i32x4 hi = *(const i32x4*)(base + swz(row, hl * 2 + 1));
+        return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
+      if constexpr (h == 0) {
+        if constexpr (NT >= 1) f.b[0][0] = ld8(sb, brow + l32);
+      } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int ra = arow[t] + l32;
-        i32x4 lo = *(const i32x4*)(sa + swz(ra, hl * 2));
-        i32x4 hi = *(const i32x4*)(sa + swz(ra, hl * 2 + 1));
-        f.a[0][t] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      }
+        for (int t = 0; t < 2; ++t) f.a[0][t] = ld8(sa, arow[t] + l32);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int rb = brow + j * 32 + l32;
-        i32x4 lo = *(const i32x4*)(sb + swz(rb, hl * 2));
-        i32x4 hi = *(const i32x4*)(sb + swz(rb, hl * 2 + 1));
-        f.b[0][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        for (int j = 1; j < NT; ++j) f.b[0][j] = ld8(sb, brow + j * 32 + l32);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int t = 0; t < 2; ++t) f.a[h][t] = *(const bf16x8*)(sa + swz(arow[t] + l32, h * 2 + hl));
 #pragma unroll
-        for (int t = 0; t < 2; ++t) f.a[kk][t] = *(const bf16x8*)(sa + swz(arow[t] + l32, kk * 2 + hl));
-#pragma unroll
-        for (int j = 0; j < NT; ++j) f.b[kk][j] = *(const bf16x8*)(sb + swz(brow + j * 32 + l32, kk * 2 + hl));
-      }
+      for (int j = 0; j < NT; ++j) f.b[h][j] = *(const bf16x8*)(sb + swz(brow + j * 32 + l32, h * 2 + hl));
     }
   };
 
@@ -221,16 +232,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     }
   }
 
-  auto mfmas = [&](const F& f, int kt, auto nt_const) {
-    constexpr int NT = decltype(nt_const)::value;
+  auto mfma_half = [&](const F& f, auto h_const, auto nt_const) {
+    constexpr int NT = decltype(nt_const)::value, h = decltype(h_const)::value;
     if constexpr (kFp8) {
+      constexpr int j0 = h == 0 ? 0 : 1, j1 = h == 0 ? (NT < 1 ? NT : 1) : NT;
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int j = j0; j < j1; ++j)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           part[t][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0][t], f.b[0][j], part[t][j], 0, 0,
                                                                         0, 127, 0, 127);
-      if (kt & 1) {   // end of a 128-deep scale block: promote
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[h][t], f.b[h][j], acc[t][j], 0, 0, 0);
+    }
+  };
+  // fp8: at the end of a 128-deep scale block (every second step) fold the
+  // block's partial sums into the accumulators with s_w(block) * s_x(row, block)
+  auto promote = [&](int kt, auto nt_const) {
+    constexpr int NT = decltype(nt_const)::value;
+    if constexpr (kFp8) {
+      if (kt & 1) {
         const int kb = kt >> 1;
         const float s0 = wscale(a.s0, a.scale_ue8m0, sw_idx0 + kb);
         const float s1 = wscale(kMode == 0 ? a.s1 : a.s0, a.scale_ue8m0, sw_idx1 + kb);
@@ -246,44 +271,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
           part[0][j] = part[1][j] = f32x16{};
         }
       }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[t][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][t], f.b[kk][j], acc[t][j], 0, 0, 0);
     }
   };
 
   auto mainloop = [&](auto nt_const) {
+    constexpr int NT = decltype(nt_const)::value;
+    constexpr std::integral_constant<int, 0> h0{};
+    constexpr std::integral_constant<int, 1> h1{};
     // prologue: K steps 0..kStages-2 in flight
 #pragma unroll
     for (int p = 0; p < kStages - 1; ++p)
       if (p < KT) issue(p, p);
-    int issued = KT < kStages - 1 ? KT : kStages - 1;
-    wait_steps<kLoads>(issued - 1);
+    wait_steps<kLoads>((KT < kStages - 1 ? KT : kStages - 1) - 1);
     __builtin_amdgcn_s_barrier();   // bare barrier: __syncthreads would wait for every step in flight
-    F cur, nxt;
-    read(0, cur, nt_const);
-    int stage = 0;
-    for (int s = 0; s + 1 < KT; ++s) {
+    F f;
+    read_half(0, f, h0, nt_const);
+    read_half(0, f, h1, nt_const);
+    wait_lgkm<0>();
+    // One K step: the MFMAs of step s, with the fragments of step s+1 read
+    // from LDS stage `next` half by half as the MFMAs free their registers.
+    auto body = [&](int s, int next) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm<kFp8 ? 0 : 2 + NT>();   // this step's first half landed
+      mfma_half(f, h0, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      read_half(next, f, h0, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm<kFp8 ? (NT >= 1 ? 2 : 0) : 2 + NT>();   // ... and its second half
+      mfma_half(f, h1, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      read_half(next, f, h1, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      promote(s, nt_const);
+    };
+    int stage = 0;                  // LDS stage of step s
+    int fill = kStages - 1;         // stage that receives step s + kStages - 1
+    int s = 0;
+    // steady state: every step refills the stage freed by step s-1, so the
+    // number of steps still in flight behind step s+1 is constant
+    for (; s < KT - (kStages - 1); ++s) {
       const int next = stage + 1 == kStages ? 0 : stage + 1;
-      wait_steps<kLoads>(issued - (s + 2));   // step s+1 landed for this thread
-      __builtin_amdgcn_s_barrier();   // ... and for all; step s-1's buffer is free
-      if (issued < KT) {
-        int stn = stage + kStages - 1;
-        stn = stn >= kStages ? stn - kStages : stn;
-        issue(stn, issued);
-        ++issued;
-      }
-      read(next, nxt, nt_const);
-      mfmas(cur, s, nt_const);
-      cur = nxt;
+      wait_vmcnt<(kStages - 3) * kLoads>();   // step s+1 landed for this thread
+      __builtin_amdgcn_s_barrier();           // ... and for all; step s-1's stage is free
+      issue(fill, s + kStages - 1);
+      fill = fill + 1 == kStages ? 0 : fill + 1;
+      body(s, next);
       stage = next;
     }
-    mfmas(cur, KT - 1, nt_const);
+    // drain: nothing left to issue
+    for (; s + 1 < KT; ++s) {
+      const int next = stage + 1 == kStages ? 0 : stage + 1;
+      wait_steps<kLoads>(KT - 2 - s);
+      __builtin_amdgcn_s_barrier();
+      body(s, next);
+      stage = next;
+    }
+    mfma_half(f, h0, nt_const);
+    mfma_half(f, h1, nt_const);
+    promote(KT - 1, nt_const);
   };
   switch (my_nt) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
@@ -339,10 +384,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
         for (int q = 0; q < 4; ++q) {
           const int ch = ch0 + q * 8 + hl * 4;
           if (ch >= N) continue;
-          uint16_t v[4];
+          float v[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = f32_to_bf16_bits(silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c]);
-          *(i32x2*)(h + ch) = i32x2{(int)(v[0] | ((uint32_t)v[1] << 16)), (int)(v[2] | ((uint32_t)v[3] << 16))};
+          for (int c = 0; c < 4; ++c) v[c] = silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c];
+          *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
         }
       }
     }
@@ -361,11 +406,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
             *(f32x4*)((float*)a.out + (int64_t)row * N + ch) =
                 f32x4{acc[t][j][q * 4 + 0], acc[t][j][q * 4 + 1], acc[t][j][q * 4 + 2], acc[t][j][q * 4 + 3]};
           } else {
-            uint16_t v[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = f32_to_bf16_bits(acc[t][j][q * 4 + c]);
+            const f32x16& y = acc[t][j];
             *(i32x2*)((uint16_t*)a.out + (int64_t)row * N + ch) =
-                i32x2{(int)(v[0] | ((uint32_t)v[1] << 16)), (int)(v[2] | ((uint32_t)v[3] << 16))};
+                i32x2{(int)pack_bf16x2(y[q * 4 + 0], y[q * 4 + 1]), (int)pack_bf16x2(y[q * 4 + 2], y[q * 4 + 3])};
           }
         }
     }

@@ -224,10 +224,10 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
         for (int q = 0; q < 4; ++q) {
           const int ch = ch0 + q * 8 + hl * 4;
           if (ch >= N) continue;
-          uint16_t v[4];
+          float v[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = f32_to_bf16_bits(silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c]);
-          *(i32x2*)(h + ch) = i32x2{(int)(v[0] | ((uint32_t)v[1] << 16)), (int)(v[2] | ((uint32_t)v[3] << 16))};
+          for (int c = 0; c < 4; ++c) v[c] = silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c];
+          *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
         }
       }
     }
@@ -246,11 +246,9 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
             *(f32x4*)((float*)a.out + (int64_t)row * N + ch) =
                 f32x4{acc[t][j][q * 4 + 0], acc[t][j][q * 4 + 1], acc[t][j][q * 4 + 2], acc[t][j][q * 4 + 3]};
           } else {
-            uint16_t v[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = f32_to_bf16_bits(acc[t][j][q * 4 + c]);
+            const f32x16& y = acc[t][j];
             *(i32x2*)((uint16_t*)a.out + (int64_t)row * N + ch) =
-                i32x2{(int)(v[0] | ((uint32_t)v[1] << 16)), (int)(v[2] | ((uint32_t)v[3] << 16))};
+                i32x2{(int)pack_bf16x2(y[q * 4 + 0], y[q * 4 + 1]), (int)pack_bf16x2(y[q * 4 + 2], y[q * 4 + 3])};
           }
         }
     }
