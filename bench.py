@@ -62,6 +62,9 @@ def parse():
                    help="only run a plain 1 GiB device copy (to scale rocprofv3 byte counters) and exit")
     p.add_argument("--layout", default="packed", choices=["packed", "rowmajor"],
                    help="expert-weight layout; packed weights are written once before timing")
+    p.add_argument("--flush", default="read", choices=["read", "write"],
+                   help="decode: evict the last-level cache between timed steps by reading (default) "
+                        "or by rewriting a 2 GiB buffer")
     return p.parse_args()
 
 
@@ -189,16 +192,31 @@ def main():
     flush = None
     if decode:
         # touched weights of a decode step fit the 256 MB last-level cache: evict it
-        # between timed steps by rewriting a 2 GiB buffer (outside the timed events)
-        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
-    moe.moe_timing_enable(True)
+        # between timed steps by streaming a 2 GiB buffer through it (outside the
+        # timed events).  Reading leaves clean lines behind; rewriting the buffer
+        # would leave dirty lines whose write-back the next step would pay for.
+        flush_buf = torch.ones(2 << 28, dtype=torch.int32, device=dev)
+        flush_sink = torch.empty((), dtype=torch.int32, device=dev)
+
+        def flush_cache():
+            if args.flush == "read":
+                torch.amax(flush_buf, dim=0, out=flush_sink)
+            else:
+                flush_buf.zero_()
+        flush = flush_cache
+    # Prefill: the library records HIP events around each of its launches
+    # during the timed steps (the gate/up kernel's duration feeds the roofline).
+    # Decode: the roofline is the whole step, timed with one event pair per
+    # step; per-launch events would add their own cost to a ~0.1 ms step, so the
+    # per-stage breakdown comes from extra steps after the timed region.
+    moe.moe_timing_enable(not decode)
     moe.moe_timing_read()
     if decode:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
-            flush.zero_()
+            flush()
             ev[i][0].record(stream)
             step()
             ev[i][1].record(stream)
@@ -216,6 +234,15 @@ def main():
         ms_per_step = elapsed_ms / args.steps
     stages = moe.moe_timing_read()
     moe.moe_timing_enable(False)
+    if decode:
+        moe.moe_timing_enable(True)
+        moe.moe_timing_read()
+        for _ in range(min(args.steps, 20)):
+            flush()
+            step()
+        torch.cuda.synchronize()
+        stages = moe.moe_timing_read()
+        moe.moe_timing_enable(False)
     value = s.T / (ms_per_step / 1e3)
     for name, (ms, n) in stages.items():
         if n:

@@ -74,8 +74,11 @@ typedef enum { MOE_ACT_NONE = 0, MOE_ACT_DYNAMIC = 1, MOE_ACT_STATIC = 2 } moe_a
  * runs tiled grouped GEMMs over the expert-sorted rows; STREAM reads every
  * touched expert's weights exactly once, split over all compute units, for
  * decode-sized batches (section "Decode-stage switching": small token counts
- * want a different scheme); it needs packed weights and T <= 64 (else
- * MOE_EUNSUPPORTED).  AUTO picks STREAM for packed weights with T <= 64. */
+ * want a different scheme); it needs packed weights and T <= 64, and for fp8
+ * experts H, I <= 8192 (else MOE_EUNSUPPORTED).  With few touched experts the
+ * K range of each weight tile is split over several workgroups and the fp32
+ * partial tiles are summed in a fixed order (results depend only on the
+ * inputs).  AUTO picks STREAM wherever it applies. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } moe_path;
 
 /* Layout of the expert weights passed to the expert GEMMs and moe_forward.
@@ -246,7 +249,10 @@ const char* moe_last_error(void);
  * its kernels with HIP events on the caller's stream.  moe_timing_read waits
  * for the recorded events, adds their elapsed times into ms[stage] and the
  * number of timed launches into launches[stage] (both host arrays of
- * MOE_NUM_STAGES entries), and clears the record.  Not thread-safe. */
+ * MOE_NUM_STAGES entries), and clears the record.  Not thread-safe.
+ * When all T*k pairs fit one 1024-pair chunk, histogram, scan and scatter run
+ * as one launch, timed under MOE_STAGE_SCAN.  A stage's time covers all of its
+ * launches (the weight-streaming GEMMs add a split-K reduction launch). */
 enum {
     MOE_STAGE_ROUTE = 0, MOE_STAGE_HIST = 1, MOE_STAGE_SCAN = 2, MOE_STAGE_SCATTER = 3,
     MOE_STAGE_QUANT_X = 4, MOE_STAGE_GATE_UP = 5, MOE_STAGE_DOWN = 6, MOE_STAGE_COMBINE = 7,

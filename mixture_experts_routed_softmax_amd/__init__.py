@@ -24,6 +24,10 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("libmoe.so is not built; run __graft_entry__.build() (or python "
                       "mixture_experts_routed_softmax_amd/_build.py) first")
 
+# torch ships its own HIP runtime; load it before libmoe so that libmoe binds to
+# the same runtime instance (and so accepts torch's streams and device state)
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---- enums (values of include/moe.h)

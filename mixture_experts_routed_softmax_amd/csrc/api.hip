@@ -105,6 +105,9 @@ moe_status validate(const moe_desc* d) {
   }
   if (d->path == MOE_PATH_STREAM && (d->w_layout != MOE_LAYOUT_PACKED || d->T > kStreamMaxTokens))
     return fail(MOE_EUNSUPPORTED, "the weight-streaming path needs packed weights and T <= %d", kStreamMaxTokens);
+  if (d->path == MOE_PATH_STREAM && d->w_dtype == MOE_DT_FP8_E4M3 &&
+      (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
+    return fail(MOE_EUNSUPPORTED, "the fp8 weight-streaming path needs H, I <= %d", 128 * kStreamMaxScaleBlocks);
   return MOE_OK;
 }
 
@@ -144,6 +147,8 @@ size_t packed_bytes(const moe_desc* d, int which) {
 
 // expert GEMMs stream the touched experts' weights (decode-sized batches)
 bool use_stream(const moe_desc* d) {
+  if (d->w_dtype == MOE_DT_FP8_E4M3 && (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
+    return false;
   return packed(d) && d->T <= kStreamMaxTokens && (d->path == MOE_PATH_STREAM || d->path == MOE_PATH_AUTO);
 }
 
@@ -160,6 +165,17 @@ int64_t sched_capacity(const moe_desc* d, int ntiles) {
   const int64_t tiles = (P + bm - 1) / bm + std::min<int64_t>(d->E, P);
   return tiles * ntiles;
 }
+
+// Weight streaming: work units (items x K splits) the launch must cover, and
+// split-K partial tiles the workspace must hold.  A split happens only below
+// kStreamTarget items, so split units stay below 2 * kStreamTarget.
+int64_t stream_units_cap(int64_t items) { return items + kStreamTarget; }
+int64_t stream_partial_units(const moe_desc* d) {
+  if (!use_stream(d)) return 0;
+  const int64_t items = std::max(sched_capacity(d, gate_up_ntiles(d)), sched_capacity(d, down_ntiles(d)));
+  return std::min<int64_t>(items * kStreamMaxSplit, 2 * kStreamTarget);
+}
+size_t stream_partial_bytes(const moe_desc* d) { return (size_t)stream_partial_units(d) * kStreamPartFloats * 4; }
 
 size_t sched_bytes(int64_t cap) { return sizeof(Schedule) + (size_t)cap * sizeof(WorkItem); }
 
@@ -203,6 +219,7 @@ struct ForwardWs {
   void* h;
   float* hs;
   void* y;
+  float* partial;
 };
 
 ForwardWs carve_forward(Carve& c, const moe_desc* d) {
@@ -224,6 +241,7 @@ ForwardWs carve_forward(Carve& c, const moe_desc* d) {
   w.h = c.take<uint8_t>((size_t)P * d->I * elt_bytes(d->w_dtype));
   if (is_fp8(d)) w.hs = c.take<float>((size_t)P * (d->I / 128));
   w.y = c.take<uint8_t>((size_t)P * d->H * elt_bytes(d->y_dtype));
+  if (use_stream(d)) w.partial = (float*)c.take<uint8_t>(stream_partial_bytes(d));
   return w;
 }
 
@@ -233,9 +251,13 @@ size_t ws_size(const moe_desc* d, int op) {
     case MOE_OP_ROUTE: return align_up(route_workspace_bytes(d->T, d->H, d->E, d->act_dtype == MOE_DT_BF16));
     case MOE_OP_PERMUTE: carve_permute(c, d, is_fp8(d)); return c.off;
     case MOE_OP_GATE_UP:
-      return d->w_dtype == MOE_DT_F32 ? 0 : align_up(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
+      return d->w_dtype == MOE_DT_F32 ? 0
+                                      : align_up(sched_bytes(sched_capacity(d, gate_up_ntiles(d)))) +
+                                            align_up(stream_partial_bytes(d));
     case MOE_OP_DOWN:
-      return d->w_dtype == MOE_DT_F32 ? 0 : align_up(sched_bytes(sched_capacity(d, down_ntiles(d))));
+      return d->w_dtype == MOE_DT_F32 ? 0
+                                      : align_up(sched_bytes(sched_capacity(d, down_ntiles(d)))) +
+                                            align_up(stream_partial_bytes(d));
     case MOE_OP_COMBINE: return 0;
     case MOE_OP_FORWARD: carve_forward(c, d); return c.off;
     default: return 0;
@@ -306,6 +328,12 @@ moe_status run_permute(const moe_desc* d, const int32_t* ids, int32_t* counts, i
                        SchedRequest s0, SchedRequest s1, hipStream_t st) {
   const int64_t P = pairs(d);
   const int64_t nb = perm_blocks(P);
+  if (nb == 1) {
+    StageTimer tm(MOE_STAGE_SCAN, st);
+    MOE_TRY_HIP(launch_permute_small(ids, P, d->E, counts, offsets, perm, inv, touched, s0, s1, st),
+                "permute launch");
+    return MOE_OK;
+  }
   {
     StageTimer tm(MOE_STAGE_HIST, st);
     MOE_TRY_HIP(launch_hist(ids, P, d->E, pw.block_counts, st), "histogram launch");
@@ -332,8 +360,9 @@ GemmArgs gemm_common(const moe_desc* d) {
 
 moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scales, const int32_t* gather,
                        const int32_t* offsets, const void* wg, const void* wu, const void* sg,
-                       const void* su, void* h, float* hs, const Schedule* sched, hipStream_t st) {
+                       const void* su, void* h, float* hs, const Schedule* sched, float* partial, hipStream_t st) {
   GemmArgs a = gemm_common(d);
+  a.partial = partial;
   a.act = act;
   a.act_scales = act_scales;
   a.gather = gather;
@@ -353,7 +382,9 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   StageTimer tm(MOE_STAGE_GATE_UP, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
-  if (use_stream(d)) e = launch_gemm_stream(a, is_fp8(d), 0, grid, st);
+  if (use_stream(d))
+    e = launch_gemm_stream(a, is_fp8(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
+                           (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), st);
   else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
@@ -363,8 +394,9 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
 }
 
 moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int32_t* offsets,
-                    const void* wd, const void* sd, void* y, const Schedule* sched, hipStream_t st) {
+                    const void* wd, const void* sd, void* y, const Schedule* sched, float* partial, hipStream_t st) {
   GemmArgs a = gemm_common(d);
+  a.partial = partial;
   a.act = h;
   a.act_scales = hs;
   a.w0 = wd;
@@ -379,7 +411,9 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   StageTimer tm(MOE_STAGE_DOWN, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
-  if (use_stream(d)) e = launch_gemm_stream(a, is_fp8(d), 1, grid, st);
+  if (use_stream(d))
+    e = launch_gemm_stream(a, is_fp8(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
+                           (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), st);
   else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);
@@ -484,8 +518,9 @@ moe_status moe_expert_gate_up_swiglu(const moe_desc* d, const void* x_sorted, co
     sched = (Schedule*)ws;
     MOE_TRY_HIP(launch_schedule(offsets, d->E, sched_req(sched, d, gate_up_ntiles(d)), st), "schedule launch");
   }
+  float* partial = sched ? (float*)((uint8_t*)ws + align_up(sched_bytes(sched_capacity(d, gate_up_ntiles(d))))) : nullptr;
   return run_gate_up(d, x_sorted, x_scales, nullptr, offsets, w_gate, w_up, w_gate_scales, w_up_scales, h,
-                     h_scales, sched, st);
+                     h_scales, sched, partial, st);
 }
 
 moe_status moe_expert_down(const moe_desc* d, const void* h, const float* h_scales, const int32_t* offsets,
@@ -506,7 +541,8 @@ moe_status moe_expert_down(const moe_desc* d, const void* h, const float* h_scal
     sched = (Schedule*)ws;
     MOE_TRY_HIP(launch_schedule(offsets, d->E, sched_req(sched, d, down_ntiles(d)), st), "schedule launch");
   }
-  return run_down(d, h, h_scales, offsets, w_down, w_down_scales, y_sorted, sched, st);
+  float* partial = sched ? (float*)((uint8_t*)ws + align_up(sched_bytes(sched_capacity(d, down_ntiles(d))))) : nullptr;
+  return run_down(d, h, h_scales, offsets, w_down, w_down_scales, y_sorted, sched, partial, st);
 }
 
 moe_status moe_unpermute_combine(const moe_desc* d, const void* y_sorted, const int32_t* inv,
@@ -571,10 +607,10 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
     act = fw.pw.xq;
     act_scales = fw.pw.xs;
   }
-  if ((s = run_gate_up(d, act, act_scales, fw.perm, fw.offsets, w_gate, w_up, sg, su, fw.h, fw.hs, fw.sched_gu,
+  if ((s = run_gate_up(d, act, act_scales, fw.perm, fw.offsets, w_gate, w_up, sg, su, fw.h, fw.hs, fw.sched_gu, fw.partial,
                        st)) != MOE_OK)
     return s;
-  if ((s = run_down(d, fw.h, fw.hs, fw.offsets, w_down, sd, fw.y, fw.sched_dn, st)) != MOE_OK) return s;
+  if ((s = run_down(d, fw.h, fw.hs, fw.offsets, w_down, sd, fw.y, fw.sched_dn, fw.partial, st)) != MOE_OK) return s;
   {
     StageTimer tm(MOE_STAGE_COMBINE, st);
     MOE_TRY_HIP(launch_combine(fw.y, d->y_dtype == MOE_DT_F32, fw.inv, w, d->T, d->k, d->H, out,

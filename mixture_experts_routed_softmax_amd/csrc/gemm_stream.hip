@@ -10,15 +10,21 @@
 //   gate/up : h[r, j] = silu(x_r . w_gate[e, j]) * (x_r . w_up[e, j])
 //   down    : y[r, o] = h_r . w_down[e, o]
 //
-// One workgroup per (touched expert, packed 256-row tile); 4 waves, each
-// owning 64 weight rows (gate/up: the gate and up rows of 32 channels) for all
-// of the expert's tokens (one or two 32-token MFMA tiles).  Weights go from
-// the contiguous packed chunks straight into registers in MFMA layout through
-// a register ring of 4 (bf16) or 3 (fp8) K steps (no LDS, no barriers); token fragments are loaded
-// from global memory (they stay in L2).  FP8: the partial sum of every
-// 64-deep step is promoted with the s_w * s_x of its 128-deep scale block; the
-// gate/up epilogue quantizes h per row over the block's 128 channels
-// (s = amax / 448).
+// Work item = (touched expert, packed 256-row tile); 4 waves, each owning 64
+// weight rows (gate/up: the gate and up rows of 32 channels) for all of the
+// expert's tokens (one or two 32-token MFMA tiles).  Weights go from the
+// contiguous packed chunks straight into registers in MFMA layout through a
+// register ring of 4 (bf16) or 3 (fp8) K steps (no LDS, no barriers); token
+// fragments are loaded from global memory (they stay in L2).  FP8: the
+// partial sum of every 64-deep step is promoted with the s_w * s_x of its
+// 128-deep scale block (both loaded with the step); the gate/up epilogue
+// quantizes h per row over the block's 128 channels (s = amax / 448).
+//
+// Split K: when there are few work items (few touched experts) each item's K
+// steps are split over S workgroups so that the stream occupies every CU;
+// the S fp32 partial tiles are summed in split order by a second launch that
+// also runs the epilogue.  S depends only on the item count, so results do
+// not depend on timing.
 #include <type_traits>
 
 #include "common.h"
@@ -47,141 +53,14 @@ struct Step {
   i32x4 b[NT][2];   // [token tile][16-byte piece]
 };
 
+// Epilogue of one work item from its fp32 accumulators.  Lane holds token
+// l32 of each token tile and channels (r/4)*8 + hl*4 + r%4 of each 32-row
+// weight tile.
 template <bool kFp8, int kMode, bool kOutF32, int NT>
-__device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& it) {
+__device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkItem& it, const f32x16 (&acc)[2][NT]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int e = it.expert;
-  const int K = a.K, N = a.N;
-  const int elt = kFp8 ? 1 : 2;
-  const int KT = K * elt / kRowB;
-
-  // weight rows (packed tile rows) of this lane
-  int arow[2];
-  if (kMode == 0) {
-    arow[0] = wave * 32 + l32;
-    arow[1] = 128 + wave * 32 + l32;
-  } else {
-    arow[0] = wave * 64 + l32;
-    arow[1] = wave * 64 + 32 + l32;
-  }
-  const uint8_t* abase = (const uint8_t*)a.w0 + ((int64_t)e * a.wtiles + it.ntile) * KT * (int64_t)kChunk;
-  // byte offsets of the two 16-byte pieces this lane needs per weight row:
-  // bf16: logical chunks 2*kk + hl (kk = 0, 1); fp8: 2*hl and 2*hl + 1
-  int aoff[2][2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) aoff[t][q] = pswz(arow[t], kFp8 ? hl * 2 + q : q * 2 + hl);
-  // token rows of this lane
-  const uint8_t* brow[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    int r = it.row_begin + j * 32 + l32;
-    r = r < it.row_end ? r : it.row_end - 1;
-    const int64_t src_row = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
-    brow[j] = (const uint8_t*)a.act + src_row * (int64_t)K * elt;
-  }
-  // byte offsets (within a K step) of the token pieces, same K mapping as A
-  int boff[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) boff[q] = (kFp8 ? hl * 2 + q : q * 2 + hl) * 16;
-
-  typedef Step<kFp8, NT> S;
-  auto load = [&](S& st, int kt) {
-    const uint8_t* ck = abase + (int64_t)kt * kChunk;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) st.a[t][q] = *(const i32x4*)(ck + aoff[t][q]);
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) st.b[j][q] = *(const i32x4*)(brow[j] + (int64_t)kt * kRowB + boff[q]);
-  };
-
-  f32x16 acc[2][NT];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[t][j] = f32x16{};
-
-  // fp8 scale bookkeeping
-  const int KB = K / 128;
-  int64_t sw0 = 0, sw1 = 0;
-  const float* sa[NT] = {};
-  if constexpr (kFp8) {
-    const int NBr = (N + 127) / 128;
-    if (kMode == 0) {
-      sw0 = ((int64_t)e * NBr + it.ntile) * KB;
-      sw1 = sw0;
-    } else {
-      int br = it.ntile * 2 + (wave >> 1);
-      br = br < NBr ? br : NBr - 1;
-      sw0 = ((int64_t)e * NBr + br) * KB;
-      sw1 = sw0;
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      int r = it.row_begin + j * 32 + l32;
-      r = r < it.row_end ? r : it.row_end - 1;
-      const int64_t src_row = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
-      sa[j] = a.act_scales + src_row * KB;
-    }
-  }
-
-  auto consume = [&](const S& st, int kt) {
-    if constexpr (kFp8) {
-      // both 64-deep halves of a 128-deep scale block carry the same scales,
-      // so each step's partial sum is promoted on its own
-      const int kb = kt >> 1;
-      const float s0 = wscale(a.s0, a.scale_ue8m0, sw0 + kb);
-      const float s1 = wscale(kMode == 0 ? a.s1 : a.s0, a.scale_ue8m0, sw1 + kb);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const i32x8 bv = {st.b[j][0].x, st.b[j][0].y, st.b[j][0].z, st.b[j][0].w,
-                          st.b[j][1].x, st.b[j][1].y, st.b[j][1].z, st.b[j][1].w};
-        const float sx = sa[j][kb];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const i32x8 av = {st.a[t][0].x, st.a[t][0].y, st.a[t][0].z, st.a[t][0].w,
-                            st.a[t][1].x, st.a[t][1].y, st.a[t][1].z, st.a[t][1].w};
-          const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, f32x16{}, 0, 0, 0, 127, 0, 127);
-          const float m = (t == 0 ? s0 : s1) * sx;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[t][j][r] = __builtin_fmaf(p[r], m, acc[t][j][r]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[t][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8)st.a[t][q], (bf16x8)st.b[j][q], acc[t][j],
-                                                                0, 0, 0);
-    }
-  };
-
-  // register ring: K steps kt .. kt+kRing-1 in flight
-  constexpr int R = kRing<kFp8>;
-  S ring[R];
-#pragma unroll
-  for (int d = 0; d < R; ++d)
-    if (d < KT) load(ring[d], d);
-  for (int kt0 = 0; kt0 < KT; kt0 += R) {
-#pragma unroll
-    for (int d = 0; d < R; ++d) {
-      const int kt = kt0 + d;
-      if (kt < KT) {
-        consume(ring[d], kt);
-        if (kt + R < KT) load(ring[d], kt + R);
-      }
-    }
-  }
-
-  // ---- epilogue
+  const int N = a.N;
   if (kMode == 0) {
     const int ch0 = it.ntile * 128 + wave * 32;
     if constexpr (kFp8) {
@@ -242,11 +121,10 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
         for (int q = 0; q < 4; ++q) {
           const int ch = it.ntile * 256 + wave * 64 + t * 32 + q * 8 + hl * 4;
           if (ch >= N) continue;
+          const f32x16& y = acc[t][j];
           if (kOutF32) {
-            *(f32x4*)((float*)a.out + (int64_t)row * N + ch) =
-                f32x4{acc[t][j][q * 4 + 0], acc[t][j][q * 4 + 1], acc[t][j][q * 4 + 2], acc[t][j][q * 4 + 3]};
+            *(f32x4*)((float*)a.out + (int64_t)row * N + ch) = f32x4{y[q * 4 + 0], y[q * 4 + 1], y[q * 4 + 2], y[q * 4 + 3]};
           } else {
-            const f32x16& y = acc[t][j];
             *(i32x2*)((uint16_t*)a.out + (int64_t)row * N + ch) =
                 i32x2{(int)pack_bf16x2(y[q * 4 + 0], y[q * 4 + 1]), (int)pack_bf16x2(y[q * 4 + 2], y[q * 4 + 3])};
           }
@@ -255,30 +133,261 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   }
 }
 
+// K steps [kt_begin, kt_end) of one work item.  With `part` the raw
+// accumulators are stored there (register i of thread tid at part[i*256+tid]);
+// otherwise the epilogue runs.
+template <bool kFp8, int kMode, bool kOutF32, int NT>
+__device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& it, int kt_begin, int kt_end,
+                                            float* part) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int e = it.expert;
+  const int K = a.K, N = a.N;
+  const int elt = kFp8 ? 1 : 2;
+  const int KT = K * elt / kRowB;
+
+  // weight rows (packed tile rows) of this lane
+  int arow[2];
+  if (kMode == 0) {
+    arow[0] = wave * 32 + l32;
+    arow[1] = 128 + wave * 32 + l32;
+  } else {
+    arow[0] = wave * 64 + l32;
+    arow[1] = wave * 64 + 32 + l32;
+  }
+  const uint8_t* abase = (const uint8_t*)a.w0 + ((int64_t)e * a.wtiles + it.ntile) * KT * (int64_t)kChunk;
+  // byte offsets of the two 16-byte pieces this lane needs per weight row:
+  // bf16: logical chunks 2*kk + hl (kk = 0, 1); fp8: 2*hl and 2*hl + 1
+  int aoff[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) aoff[t][q] = pswz(arow[t], kFp8 ? hl * 2 + q : q * 2 + hl);
+  // token rows of this lane
+  int64_t src_row[NT];
+  const uint8_t* brow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    int r = it.row_begin + j * 32 + l32;
+    r = r < it.row_end ? r : it.row_end - 1;
+    src_row[j] = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
+    brow[j] = (const uint8_t*)a.act + src_row[j] * (int64_t)K * elt;
+  }
+  // byte offsets (within a K step) of the token pieces, same K mapping as A
+  int boff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) boff[q] = (kFp8 ? hl * 2 + q : q * 2 + hl) * 16;
+
+  const int KB = K / 128;
+
+  typedef Step<kFp8, NT> S;
+  auto load = [&](S& st, int kt) {
+    const uint8_t* ck = abase + (int64_t)kt * kChunk;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) st.a[t][q] = *(const i32x4*)(ck + aoff[t][q]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) st.b[j][q] = *(const i32x4*)(brow[j] + (int64_t)kt * kRowB + boff[q]);
+  };
+
+  f32x16 acc[2][NT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = f32x16{};
+
+  // fp8 scales of the whole K range, staged in LDS once: activation scales of
+  // the item's rows (s_sx[row][kb]) and the block scales of the weight rows
+  // (gate/up: s_sw[0] gate, s_sw[1] up; down: s_sw[h] for the tile's half h)
+  __shared__ float s_sx[kFp8 ? kStreamMaxTokens * kStreamMaxScaleBlocks : 1];
+  __shared__ float s_sw[2][kFp8 ? kStreamMaxScaleBlocks : 1];
+  auto stage_scales = [&]() {
+    if constexpr (kFp8) {
+      const int NBr = (N + 127) / 128;
+      for (int i = tid; i < kStreamMaxTokens * KB; i += 256) {
+        const int row = i / KB, kb = i - row * KB;
+        int r = it.row_begin + row;
+        r = r < it.row_end ? r : it.row_end - 1;
+        const int64_t src = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
+        s_sx[i] = a.act_scales[src * KB + kb];
+      }
+      for (int i = tid; i < 2 * KB; i += 256) {
+        const int h = i / KB, kb = i - h * KB;
+        if (kMode == 0) {
+          s_sw[h][kb] = wscale(h == 0 ? a.s0 : a.s1, a.scale_ue8m0, ((int64_t)e * NBr + it.ntile) * KB + kb);
+        } else {
+          int br = it.ntile * 2 + h;
+          br = br < NBr ? br : NBr - 1;
+          s_sw[h][kb] = wscale(a.s0, a.scale_ue8m0, ((int64_t)e * NBr + br) * KB + kb);
+        }
+      }
+      __syncthreads();
+    }
+  };
+
+  auto consume = [&](const S& st, int kt) {
+    if constexpr (kFp8) {
+      // each step's partial sum is promoted on its own (both 64-deep halves
+      // of a 128-deep scale block carry the same scales)
+      const int kb = kt >> 1;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const i32x8 bv = {st.b[j][0].x, st.b[j][0].y, st.b[j][0].z, st.b[j][0].w,
+                          st.b[j][1].x, st.b[j][1].y, st.b[j][1].z, st.b[j][1].w};
+        const float sx = s_sx[(j * 32 + l32) * KB + kb];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const i32x8 av = {st.a[t][0].x, st.a[t][0].y, st.a[t][0].z, st.a[t][0].w,
+                            st.a[t][1].x, st.a[t][1].y, st.a[t][1].z, st.a[t][1].w};
+          const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, f32x16{}, 0, 0, 0, 127, 0, 127);
+          const float m = s_sw[kMode == 0 ? t : (wave >> 1)][kb] * sx;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][j][r] = __builtin_fmaf(p[r], m, acc[t][j][r]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[t][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8)st.a[t][q], (bf16x8)st.b[j][q], acc[t][j],
+                                                                0, 0, 0);
+    }
+  };
+
+  // register ring: K steps kt .. kt+kRing-1 in flight
+  constexpr int R = kRing<kFp8>;
+  S ring[R];
+  int kt0 = kt_begin;
+  if (kt_end - kt_begin >= 2 * R) {
+    // steady state: every slot is consumed and refilled with no conditions
+    // (prologue included), so each wait knows exactly how many loads are
+    // younger than the slot's own
+#pragma unroll
+    for (int d = 0; d < R; ++d) load(ring[d], kt_begin + d);
+    stage_scales();
+    for (; kt0 + 2 * R <= kt_end; kt0 += R) {
+#pragma unroll
+      for (int d = 0; d < R; ++d) {
+        consume(ring[d], kt0 + d);
+        load(ring[d], kt0 + d + R);
+        __builtin_amdgcn_sched_barrier(0);   // keep the slots in ring order
+      }
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < R; ++d)
+      if (kt_begin + d < kt_end) load(ring[d], kt_begin + d);
+    stage_scales();
+  }
+  for (; kt0 < kt_end; kt0 += R) {
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+      const int kt = kt0 + d;
+      if (kt < kt_end) {
+        consume(ring[d], kt);
+        if (kt + R < kt_end) load(ring[d], kt + R);
+      }
+    }
+  }
+
+  if (part != nullptr) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[((t * NT + j) * 16 + r) * 256 + tid] = acc[t][j][r];
+    return;
+  }
+  stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
+}
+
 template <bool kFp8, int kMode, bool kOutF32>
 __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a) {
-  const int w = xcd_work_index(a.sched->total);
-  if (w < 0) return;
+  const int items = a.sched->total;
+  const int KT = a.K * (kFp8 ? 1 : 2) / kRowB;
+  const int S = stream_splits(items, KT);
+  const int u = xcd_work_index(items * S);
+  if (u < 0) return;
+  const int w = u / S, sp = u - w * S;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
+  const int kt0 = (int)((int64_t)KT * sp / S), kt1 = (int)((int64_t)KT * (sp + 1) / S);
+  float* part = S > 1 ? a.partial + (int64_t)u * kStreamPartFloats : nullptr;
   if (it.row_end - it.row_begin > 32)
-    stream_tile<kFp8, kMode, kOutF32, 2>(a, it);
+    stream_tile<kFp8, kMode, kOutF32, 2>(a, it, kt0, kt1, part);
   else
-    stream_tile<kFp8, kMode, kOutF32, 1>(a, it);
+    stream_tile<kFp8, kMode, kOutF32, 1>(a, it, kt0, kt1, part);
+}
+
+// Split-K reduction: one workgroup per work item sums its S partial tiles in
+// split order, then runs the epilogue.  Nothing to do when S == 1.
+template <bool kFp8, int kMode, bool kOutF32, int NT>
+__device__ __forceinline__ void stream_reduce(const GemmArgs& a, const WorkItem& it, const float* part, int S) {
+  f32x16 acc[2][NT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = f32x16{};
+  for (int sp = 0; sp < S; ++sp) {
+    const float* p = part + (int64_t)sp * kStreamPartFloats + threadIdx.x;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][j][r] += p[((t * NT + j) * 16 + r) * 256];
+  }
+  stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
+}
+
+template <bool kFp8, int kMode, bool kOutF32>
+__global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
+  const int items = a.sched->total;
+  const int KT = a.K * (kFp8 ? 1 : 2) / kRowB;
+  const int S = stream_splits(items, KT);
+  const int w = blockIdx.x;
+  if (S == 1 || w >= items) return;
+  const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
+  const float* part = a.partial + (int64_t)w * S * kStreamPartFloats;
+  if (it.row_end - it.row_begin > 32)
+    stream_reduce<kFp8, kMode, kOutF32, 2>(a, it, part, S);
+  else
+    stream_reduce<kFp8, kMode, kOutF32, 1>(a, it, part, S);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream) {
+hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, int reduce_grid, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
-  dim3 g(grid), b(256);
+  dim3 g(grid), rg(reduce_grid), b(256);
   if (fp8) {
-    if (mode == 0) hipLaunchKernelGGL((gemm_stream_kernel<true, 0, false>), g, b, 0, stream, a);
-    else if (a.out_f32) hipLaunchKernelGGL((gemm_stream_kernel<true, 1, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_stream_kernel<true, 1, false>), g, b, 0, stream, a);
+    if (mode == 0) {
+      hipLaunchKernelGGL((gemm_stream_kernel<true, 0, false>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((stream_reduce_kernel<true, 0, false>), rg, b, 0, stream, a);
+    } else if (a.out_f32) {
+      hipLaunchKernelGGL((gemm_stream_kernel<true, 1, true>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((stream_reduce_kernel<true, 1, true>), rg, b, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((gemm_stream_kernel<true, 1, false>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((stream_reduce_kernel<true, 1, false>), rg, b, 0, stream, a);
+    }
   } else {
-    if (mode == 0) hipLaunchKernelGGL((gemm_stream_kernel<false, 0, false>), g, b, 0, stream, a);
-    else if (a.out_f32) hipLaunchKernelGGL((gemm_stream_kernel<false, 1, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_stream_kernel<false, 1, false>), g, b, 0, stream, a);
+    if (mode == 0) {
+      hipLaunchKernelGGL((gemm_stream_kernel<false, 0, false>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((stream_reduce_kernel<false, 0, false>), rg, b, 0, stream, a);
+    } else if (a.out_f32) {
+      hipLaunchKernelGGL((gemm_stream_kernel<false, 1, true>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((stream_reduce_kernel<false, 1, true>), rg, b, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((gemm_stream_kernel<false, 1, false>), g, b, 0, stream, a);
+      hipLaunchKernelGGL((stream_reduce_kernel<false, 1, false>), rg, b, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -37,6 +37,10 @@ hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int3
                        SchedRequest s0, SchedRequest s1, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* block_base,
                           int32_t* perm, int32_t* inv, hipStream_t stream);
+// hist + scan + scatter in one workgroup, for P <= kPermChunk
+hipError_t launch_permute_small(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* touched, SchedRequest s0, SchedRequest s1,
+                                hipStream_t stream);
 // schedule from offsets alone (staged entry points)
 hipError_t launch_schedule(const int32_t* offsets, int E, SchedRequest s, hipStream_t stream);
 
@@ -72,6 +76,7 @@ struct GemmArgs {
   int E;
   int64_t P;
   int wtiles;               // packed weights: row tiles per expert
+  float* partial;           // weight streaming: split-K partial tiles
 };
 
 // tile geometry of the grouped GEMMs
@@ -90,9 +95,26 @@ hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_packed(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
 constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
-// weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per touched expert)
-hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream);
+// weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per
+// touched expert), split over K when there are few items, plus its split-K
+// reduction launch (reduce_grid >= min(item capacity, kStreamTarget): only
+// fewer than kStreamTarget items are ever split)
+hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, int reduce_grid, hipStream_t stream);
 constexpr int kStreamMaxTokens = 64;
+constexpr int kStreamMaxScaleBlocks = 64;   // fp8 streaming: K / 128 at most (K <= 8192)
+constexpr int kStreamTarget = 1024;      // work units the split aims for (two rounds of 2 per CU)
+constexpr int kStreamMaxSplit = 16;
+constexpr int kStreamMinSteps = 4;       // K steps per split at least
+constexpr int kStreamPartFloats = 2 * 2 * 16 * 256;   // fp32 partial tile of one work unit
+// K splits per work item for `items` items of KT steps (host and device agree)
+__host__ __device__ inline int stream_splits(int items, int KT) {
+  if (items <= 0 || items >= kStreamTarget) return 1;
+  int smax = KT / kStreamMinSteps;
+  smax = smax < kStreamMaxSplit ? smax : kStreamMaxSplit;
+  smax = smax < 1 ? 1 : smax;
+  const int s = (kStreamTarget + items - 1) / items;
+  return s < smax ? s : smax;
+}
 constexpr int kPackedTokBf16 = 256;          // token rows per packed bf16 tile
 constexpr int kPackedTokFp8 = 128;           // token rows per packed fp8 tile
 

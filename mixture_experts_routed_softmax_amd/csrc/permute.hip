@@ -13,6 +13,7 @@
 //   scan    : counts, offsets, per-chunk bases (offsets + earlier chunks), the
 //             touched-expert list and the grouped-GEMM work schedules
 //   scatter : stable in-chunk ranks (wave readlane scan + per-wave counts)
+// or, when all pairs fit one chunk, a single workgroup that does all three.
 #include "common.h"
 #include "kernels.h"
 
@@ -147,6 +148,63 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   if (s1.sched != nullptr) build_schedule(s_offsets, E, s1, s_tiles, s_items, s_tmp);
 }
 
+// All of the above in one workgroup when the pairs fit one chunk (P <= 1024,
+// e.g. decode batches): histogram, counts and offsets, stable ranks, the
+// touched-expert list and the schedules, with a single launch.
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ touched, SchedRequest s0,
+    SchedRequest s1) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_wcount[16][kMaxExperts];
+  __shared__ int s_offsets[kMaxExperts + 1];
+  __shared__ int s_tiles[kMaxExperts];
+  __shared__ int s_items[kMaxExperts + 1];
+  __shared__ int s_tmp[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int x = tid; x < E; x += 1024) s_cnt[x] = 0;
+  for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
+  __syncthreads();
+  int e = tid < P ? ids[tid] : -1;
+  if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
+  // rank among earlier lanes of this wave with the same expert
+  int rank = 0;
+  for (int j = 0; j < 64; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    rank += (j < lane && ej == e) ? 1 : 0;
+  }
+  if (e >= 0) {
+    atomicAdd(&s_cnt[e], 1);
+    atomicAdd(&s_wcount[wave][e], 1);
+  }
+  __syncthreads();
+  if (tid < E) {
+    s_offsets[tid] = s_cnt[tid];
+    counts[tid] = s_cnt[tid];
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_offsets, E, s_tmp);
+  if (tid == 0) s_offsets[E] = total;
+  __syncthreads();
+  for (int x = tid; x <= E; x += 1024) offsets[x] = s_offsets[x];
+  if (e >= 0) {
+    int row = s_offsets[e] + rank;
+    for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
+    perm[row] = tid;
+    inv[tid] = row;
+  }
+  if (touched != nullptr) {
+    if (tid < E) s_tiles[tid] = (s_offsets[tid + 1] - s_offsets[tid]) > 0 ? 1 : 0;
+    __syncthreads();
+    const int U = block_exclusive_scan(s_tiles, E, s_tmp);
+    if (tid < E && s_offsets[tid + 1] > s_offsets[tid]) touched[s_tiles[tid]] = tid;
+    if (tid == 0) touched[E] = U;
+    __syncthreads();
+  }
+  if (s0.sched != nullptr) build_schedule(s_offsets, E, s0, s_tiles, s_items, s_tmp);
+  if (s1.sched != nullptr) build_schedule(s_offsets, E, s1, s_tiles, s_items, s_tmp);
+}
+
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         SchedRequest rq) {
   __shared__ int s_offsets[kMaxExperts + 1];
@@ -265,6 +323,15 @@ hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* b
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(256), 0, stream, ids, P, E,
                      block_base, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_small(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* touched, SchedRequest s0, SchedRequest s1,
+                                hipStream_t stream) {
+  if (P > kPermChunk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)P, E, counts, offsets, perm,
+                     inv, touched, s0, s1);
   return hipGetLastError();
 }
 
