@@ -133,9 +133,9 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
   }
 }
 
-// K steps [kt_begin, kt_end) of one work item.  With `part` the raw
-// accumulators are stored there (register i of thread tid at part[i*256+tid]);
-// otherwise the epilogue runs.
+// K steps [kt_begin, kt_end) of one work item.  With `part` the fp32
+// accumulators of the item's valid rows are stored there; otherwise the
+// epilogue runs.
 template <bool kFp8, int kMode, bool kOutF32, int NT>
 __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& it, int kt_begin, int kt_end,
                                             float* part) {
@@ -297,12 +297,20 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   }
 
   if (part != nullptr) {
+    // partial tile, token-row major: part[row * 256 + channel of the 256-row
+    // weight tile]; only the item's valid rows are written
+    const int rows = it.row_end - it.row_begin;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int j = 0; j < NT; ++j) {
+      if (j * 32 + l32 >= rows) continue;
+      float* prow = part + (j * 32 + l32) * 256 + wave * 64 + hl * 4;
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part[((t * NT + j) * 16 + r) * 256 + tid] = acc[t][j][r];
+        for (int q = 0; q < 4; ++q)
+          *(f32x4*)(prow + t * 32 + q * 8) =
+              f32x4{acc[t][j][q * 4 + 0], acc[t][j][q * 4 + 1], acc[t][j][q * 4 + 2], acc[t][j][q * 4 + 3]};
+    }
     return;
   }
   stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
@@ -326,26 +334,10 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a) {
 }
 
 // Split-K reduction: one workgroup per work item sums its S partial tiles in
-// split order, then runs the epilogue.  Nothing to do when S == 1.
-template <bool kFp8, int kMode, bool kOutF32, int NT>
-__device__ __forceinline__ void stream_reduce(const GemmArgs& a, const WorkItem& it, const float* part, int S) {
-  f32x16 acc[2][NT];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[t][j] = f32x16{};
-  for (int sp = 0; sp < S; ++sp) {
-    const float* p = part + (int64_t)sp * kStreamPartFloats + threadIdx.x;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][j][r] += p[((t * NT + j) * 16 + r) * 256];
-  }
-  stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
-}
-
+// split order and runs the epilogue, one thread per (row, output channel).
+// Nothing to do when S == 1.  Partial tile layout: part[row * 256 + c] with,
+// for gate/up, the gate value of channel ntile*128 + w*32 + x at c = w*64 + x
+// and its up value at c = w*64 + 32 + x; for down, channel ntile*256 + c.
 template <bool kFp8, int kMode, bool kOutF32>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
   const int items = a.sched->total;
@@ -354,11 +346,79 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
   const int w = blockIdx.x;
   if (S == 1 || w >= items) return;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
+  const int rows = it.row_end - it.row_begin;
   const float* part = a.partial + (int64_t)w * S * kStreamPartFloats;
-  if (it.row_end - it.row_begin > 32)
-    stream_reduce<kFp8, kMode, kOutF32, 2>(a, it, part, S);
-  else
-    stream_reduce<kFp8, kMode, kOutF32, 1>(a, it, part, S);
+  const int tid = threadIdx.x, N = a.N;
+  // sums of the S (<= kStreamMaxSplit) partials at offsets o0 and o1, in
+  // split order; all loads are issued before the first add
+  auto total2 = [&](int o0, int o1, float& z0, float& z1) {
+    float v0[kStreamMaxSplit], v1[kStreamMaxSplit];
+#pragma unroll
+    for (int u = 0; u < kStreamMaxSplit; ++u) {
+      v0[u] = u < S ? part[(int64_t)u * kStreamPartFloats + o0] : 0.f;
+      v1[u] = u < S ? part[(int64_t)u * kStreamPartFloats + o1] : 0.f;
+    }
+    z0 = 0.f;
+    z1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < kStreamMaxSplit; ++u) {
+      z0 += v0[u];
+      z1 += v1[u];
+    }
+  };
+  if (kMode == 0) {
+    // 128 channels per row: two waves per row, rows two at a time
+    for (int base = 0; base < rows * 128; base += 256) {
+      const int idx = base + tid;
+      const int row = idx >> 7, c = idx & 127;
+      const bool live = row < rows;
+      float hv = 0.f;
+      if (live) {
+        const int o = row * 256 + (c >> 5) * 64 + (c & 31);
+        float g, u;
+        total2(o, o + 32, g, u);
+        hv = silu(g) * u;
+      }
+      const int ch = it.ntile * 128 + c;
+      if constexpr (kFp8) {
+        // per-row quantization over the 128 channels (one activation group)
+        __shared__ float s_m[4];
+        float m = fabsf(hv);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if ((tid & 63) == 0) s_m[tid >> 6] = m;
+        __syncthreads();
+        const float amax = fmaxf(s_m[(tid >> 7) * 2], s_m[(tid >> 7) * 2 + 1]);
+        __syncthreads();
+        if (live) {
+          const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+          const int64_t r = it.row_begin + row;
+          ((uint8_t*)a.out)[r * N + ch] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(hv / sc, 0.f, 0, false) & 0xff);
+          if (c == 0) a.out_scales[r * (N / 128) + it.ntile] = sc;
+        }
+      } else {
+        if (live && ch < N) ((uint16_t*)a.out)[(int64_t)(it.row_begin + row) * N + ch] = f32_to_bf16_bits(hv);
+      }
+    }
+  } else {
+    // two rows per pass
+    for (int idx = tid; idx < rows * 256; idx += 512) {
+      const int row = idx >> 8, c = idx & 255;
+      const bool second = row + 1 < rows;
+      float y, y2;
+      total2(row * 256 + c, (second ? row + 1 : row) * 256 + c, y, y2);
+      const int ch = it.ntile * 256 + c;
+      if (ch >= N) continue;
+      if (second) {
+        const int64_t o2 = (int64_t)(it.row_begin + row + 1) * N + ch;
+        if (kOutF32) ((float*)a.out)[o2] = y2;
+        else ((uint16_t*)a.out)[o2] = f32_to_bf16_bits(y2);
+      }
+      const int64_t o = (int64_t)(it.row_begin + row) * N + ch;
+      if (kOutF32) ((float*)a.out)[o] = y;
+      else ((uint16_t*)a.out)[o] = f32_to_bf16_bits(y);
+    }
+  }
 }
 
 }  // namespace

@@ -41,19 +41,29 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
 }
 
 // In-place exclusive scan of v[0..n) (n <= 1024) by the whole 1024-thread block;
-// returns the total.  v must be in LDS; tmp is LDS scratch of 1024 ints.
+// returns the total.  v must be in LDS; tmp is LDS scratch of at least 16 ints.
+// Each wave scans its 64 entries with lane shuffles, then the 16 wave totals
+// are scanned the same way by every wave.
 __device__ int block_exclusive_scan(int* v, int n, int* tmp) {
-  const int tid = threadIdx.x;
-  tmp[tid] = tid < n ? v[tid] : 0;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int x = tid < n ? v[tid] : 0;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
   }
-  int total = tmp[1023];
-  if (tid < n) v[tid] = tmp[tid] - v[tid];
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int wt = lane < 16 ? tmp[lane] : 0;   // wave totals, scanned inclusively
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const int y = __shfl_up(wt, off);
+    if (lane >= off) wt += y;
+  }
+  const int before = wave > 0 ? __shfl(wt, wave - 1) : 0;
+  const int total = __shfl(wt, 15);
+  if (tid < n) v[tid] = before + inc - x;
   __syncthreads();
   return total;
 }

@@ -194,14 +194,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   if (tok >= T) return;
   float key[4];
   bool taken[4];
+  // Slices are added in ascending order; the loads of 8 slices are issued
+  // together so that their latencies overlap.
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sl0 = 0; sl0 < slices; sl0 += 8) {
+    float v[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[q][u] = (e < E && sl0 + u < slices) ? part[((int64_t)(sl0 + u) * T + tok) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) z[q] += v[q][u];
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     taken[q] = !(e < E);
-    float z = 0.f;
-    if (e < E)
-      for (int sl = 0; sl < slices; ++sl) z += part[((int64_t)sl * T + tok) * E + e];
-    key[q] = e < E ? z + (bias ? bias[e] : 0.f) : -INFINITY;
+    key[q] = e < E ? z[q] + (bias ? bias[e] : 0.f) : -INFINITY;
   }
   select_topk(key, taken, lane, E, k, score, renorm, routed_scale, ids_out + tok * k, w_out + tok * k);
 }
