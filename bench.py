@@ -62,6 +62,9 @@ def parse():
                    help="only run a plain 1 GiB device copy (to scale rocprofv3 byte counters) and exit")
     p.add_argument("--layout", default="packed", choices=["packed", "rowmajor"],
                    help="expert-weight layout; packed weights are written once before timing")
+    p.add_argument("--graph", default="off", choices=["auto", "off"],
+                   help="decode: replay each timed step as a captured HIP graph (auto) or launch eagerly "
+                        "(off, the default: measured faster on this stack)")
     p.add_argument("--flush", default="read", choices=["read", "write"],
                    help="decode: evict the last-level cache between timed steps by reading (default) "
                         "or by rewriting a 2 GiB buffer")
@@ -181,14 +184,25 @@ def main():
     ws = moe.workspace(d, moe.MOE_OP_FORWARD, dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step():   # on the current stream (the capture stream while a graph is recorded)
         moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], wg, wu, dn, L.get("s_gate"),
-                        L.get("s_up"), L.get("s_down"), out, None, None, counts, ws, stream)
+                        L.get("s_up"), L.get("s_down"), out, None, None, counts, ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     decode = s.T <= 64
+    run = step
+    graph = None
+    if decode and args.graph != "off":
+        # A decode step is a chain of short kernels: replay it as one HIP graph
+        # (the library only enqueues work, so the whole forward is capturable).
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
     flush = None
     if decode:
         # touched weights of a decode step fit the 256 MB last-level cache: evict it
@@ -218,7 +232,7 @@ def main():
         for i in range(args.steps):
             flush()
             ev[i][0].record(stream)
-            step()
+            run()
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         times = sorted(a.elapsed_time(b) for a, b in ev)
@@ -258,7 +272,8 @@ def main():
         achieved = alg_bytes / (ms_per_step / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "moe_forward (whole step, median of %d individually timed steps)" % args.steps,
+                "kernel": "moe_forward (whole step%s, median of %d individually timed steps)"
+                          % (", replayed as a HIP graph" if graph is not None else "", args.steps),
                 "alg_bytes_per_launch": alg_bytes, "touched_experts": touched}
     else:
         ms_gu, n_gu = stages["gate_up"]

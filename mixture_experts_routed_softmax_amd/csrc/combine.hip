@@ -2,7 +2,8 @@
 // paragraph: the expert outputs are aggregated with the routing weights):
 //   out[t, :] = sum_{i<k} w[t, i] * y_sorted[inv[t*k + i], :]
 // fp32 sums in slot order, one rounding to the output type, no atomics.
-// One workgroup per token, 8 channels (16-byte bf16 loads) per thread step.
+// One workgroup per (token, 2048 channels), 8 channels (one 16-byte bf16
+// load per slot) per thread; the loads of up to 8 slots are issued together.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,26 +24,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     s_w[threadIdx.x] = w[t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < H / 8; c += 256) {
+  const int c = blockIdx.y * 256 + threadIdx.x;   // group of 8 channels
+  if (c < H / 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < k; ++i) {
-      const float wi = s_w[i];
-      const int64_t base = (int64_t)s_row[i] * H + c * 8;
-      if (kYF32) {
-        const f32x4 v0 = *(const f32x4*)((const float*)y + base);
-        const f32x4 v1 = *(const f32x4*)((const float*)y + base + 4);
+    for (int i0 = 0; i0 < k; i0 += 8) {
+      // the loads of 8 slots first, then the slot-ordered accumulation
+      f32x4 v0[8], v1[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[q] = __builtin_fmaf(wi, v0[q], acc[q]);
-          acc[4 + q] = __builtin_fmaf(wi, v1[q], acc[4 + q]);
+      for (int u = 0; u < 8; ++u) {
+        v0[u] = f32x4{};
+        v1[u] = f32x4{};
+        if (i0 + u < k) {
+          const int64_t base = (int64_t)s_row[i0 + u] * H + c * 8;
+          if (kYF32) {
+            v0[u] = *(const f32x4*)((const float*)y + base);
+            v1[u] = *(const f32x4*)((const float*)y + base + 4);
+          } else {
+            v0[u] = __builtin_bit_cast(f32x4, *(const i32x4*)((const uint16_t*)y + base));
+          }
         }
-      } else {
-        const i32x4 v = *(const i32x4*)((const uint16_t*)y + base);
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t two = (uint32_t)v[q];
-          acc[2 * q] = __builtin_fmaf(wi, bf16_bits_to_f32((uint16_t)(two & 0xffff)), acc[2 * q]);
-          acc[2 * q + 1] = __builtin_fmaf(wi, bf16_bits_to_f32((uint16_t)(two >> 16)), acc[2 * q + 1]);
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u >= k) break;
+        const float wi = s_w[i0 + u];
+        if (kYF32) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[q] = __builtin_fmaf(wi, v0[u][q], acc[q]);
+            acc[4 + q] = __builtin_fmaf(wi, v1[u][q], acc[4 + q]);
+          }
+        } else {
+          const i32x4 v = __builtin_bit_cast(i32x4, v0[u]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t two = (uint32_t)v[q];
+            acc[2 * q] = __builtin_fmaf(wi, bf16_bits_to_f32((uint16_t)(two & 0xffff)), acc[2 * q]);
+            acc[2 * q + 1] = __builtin_fmaf(wi, bf16_bits_to_f32((uint16_t)(two >> 16)), acc[2 * q + 1]);
+          }
         }
       }
     }
@@ -65,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const float* w, int64_t T,
                           int k, int H, void* out, int out_f32, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)T), block(256);
+  dim3 grid((unsigned)T, (unsigned)((H / 8 + 255) / 256)), block(256);
   if (y_f32 && out_f32)
     hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, stream, y, inv, w, k, H, out);
   else if (y_f32)

@@ -295,7 +295,9 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __r
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int groups = n / 128;
-  for (int g = wave; g < groups; g += 4) {
+  {
+    const int g = blockIdx.y * 4 + wave;   // one 128-channel group per wave
+    if (g >= groups) return;
     const uint32_t two = *(const uint32_t*)(x + row * n + g * 128 + 2 * lane);
     float a = bf16_bits_to_f32((uint16_t)(two & 0xffff));
     float b = bf16_bits_to_f32((uint16_t)(two >> 16));
@@ -370,8 +372,8 @@ hipError_t launch_gather_scales(const float* src, const int32_t* perm, int k, in
 hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int64_t rows, int n, uint8_t* codes,
                                  float* scales, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x_bf16, n,
-                     codes, scales);
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows, (unsigned)((n / 128 + 3) / 4)), dim3(256), 0,
+                     stream, x_bf16, n, codes, scales);
   return hipGetLastError();
 }
 
