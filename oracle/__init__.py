@@ -26,6 +26,7 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 F32, BF16, E4M3 = 0, 1, 2
 SOFTMAX, SIGMOID = 0, 1
 SCALE_NONE, SCALE_F32, SCALE_UE8M0 = 0, 1, 2
+GATE_SILU, GATE_GELU, GATE_RELU = 0, 1, 2    # SwiGLU / GeGLU / ReGLU
 
 
 def build(force: bool = False) -> str:
@@ -45,7 +46,7 @@ _lib = None
 class _Experts(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("wdt", ctypes.c_int32), ("scale_fmt", ctypes.c_int32),
-                ("block", ctypes.c_int32), ("act_fp8", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("act_fp8", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
 
@@ -203,7 +204,8 @@ class Experts:
     (torch CPU tensors or numpy float32 / uint16 bits / uint8 codes).  For fp8,
     s_gate, s_up [E,I/b,H/b] and s_down [E,H/b,I/b] are float32 (SCALE_F32) or
     uint8 E8M0 bytes (SCALE_UE8M0), and act_fp8 turns on the dynamic per-row
-    activation quantization."""
+    activation quantization.  gate picks the gated activation (section
+    "SonicMoE" of "Experts backends": silu, gelu or relu)."""
     w_gate: object
     w_up: object
     w_down: object
@@ -213,6 +215,7 @@ class Experts:
     scale_fmt: int = SCALE_NONE
     block: int = 128
     act_fp8: bool = False
+    gate: int = 0            # GATE_SILU, GATE_GELU or GATE_RELU
 
     def __post_init__(self):
         self._arrs = []
@@ -230,7 +233,7 @@ class Experts:
         self._arrs = [g, u, d, sg, su, sd]
         self.E, self.I, self.H = E, I, H
         self._st = _Experts(H, I, E, gf, self.scale_fmt if gf == E4M3 else SCALE_NONE,
-                            self.block, int(bool(self.act_fp8)), 0,
+                            self.block, int(bool(self.act_fp8)), int(self.gate),
                             g.ctypes.data, u.ctypes.data, d.ctypes.data,
                             None if sg is None else sg.ctypes.data,
                             None if su is None else su.ctypes.data,

@@ -14,8 +14,8 @@
  *   - backend table, rows grouped_mm / deepgemm: tokens are ordered by their
  *     selected expert before one grouped GEMM;
  *   - backend table, row deepgemm_megamoe, and section "SonicMoE": each expert is
- *     a gated MLP -- up projection, SwiGLU (gated activation silu), down
- *     projection;
+ *     a gated MLP -- up projection, gated activation, down projection; the
+ *     gate is silu, gelu or relu (SwiGLU / GeGLU / ReGLU, section "SonicMoE");
  *   - paragraph under the backend table and section "FP8 and FP4 quantized
  *     experts": FP8 experts carry float32 or UE8M0 block scales, and activations
  *     are quantized with dynamic per-row scales (static per-tensor scales are
@@ -29,7 +29,10 @@
  *   - optional renormalisation of the k selected scores to sum 1, then a
  *     multiplicative routed scale;
  *   - stable order within an expert: ascending (token, slot);
- *   - SwiGLU: a_j = silu(g_j) * u_j with g = x W_gate^T, u = x W_up^T, no biases;
+ *   - gated activation: a_j = act(g_j) * u_j with g = x W_gate^T, u = x W_up^T,
+ *     no biases; silu(g) = g / (1 + e^-g), gelu(g) = g * Phi(g) with Phi the
+ *     standard normal CDF (the exact form, 0.5 g (1 + erf(g / sqrt 2)); the
+ *     page names gelu without saying which form), relu(g) = max(g, 0);
  *   - routing weight applied after the down projection;
  *   - FP8: OCP e4m3 ("fn": no infinities, 0x7f/0xff are NaN, max 448), weight
  *     block 128 x 128, activation group = 128 consecutive channels of one row,
@@ -55,6 +58,8 @@ enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };
 /* fp8 weight-scale formats */
 enum { ORC_SCALE_NONE = 0, ORC_SCALE_F32 = 1, ORC_SCALE_UE8M0 = 2 };
+/* gate activation of the gated MLP */
+enum { ORC_GATE_SILU = 0, ORC_GATE_GELU = 1, ORC_GATE_RELU = 2 };
 
 /* ------------------------------------------------------------------ decoders */
 
@@ -246,7 +251,7 @@ typedef struct {
     int32_t scale_fmt;  /* ORC_SCALE_*; used only with ORC_E4M3 */
     int32_t block;      /* weight block edge and activation group size (fp8) */
     int32_t act_fp8;    /* quantize x and a per row per `block` channels */
-    int32_t pad_;
+    int32_t gate;       /* ORC_GATE_* */
     const void *w_gate; /* [E, I, H] */
     const void *w_up;   /* [E, I, H] */
     const void *w_down; /* [E, H, I] */
@@ -279,8 +284,16 @@ static void quant_row(const orc_experts *W, const double *v, int n, double *out)
         orc_quant_group(v + g, W->block, out + g, NULL, NULL);
 }
 
+/* gate activation (section "SonicMoE": silu, gelu or relu) */
+static double gate_act(int gate, double g)
+{
+    if (gate == ORC_GATE_GELU) return 0.5 * g * (1.0 + erf(g / sqrt(2.0)));
+    if (gate == ORC_GATE_RELU) return g > 0.0 ? g : 0.0;
+    return g / (1.0 + exp(-g));
+}
+
 /* Gated MLP of expert e on one row xin[H]:
- *   x^ = Q(x) (fp8 only), g = W_gate x^, u = W_up x^, a = silu(g) * u,
+ *   x^ = Q(x) (fp8 only), g = W_gate x^, u = W_up x^, a = act(g) * u,
  *   a^ = Q(a) (fp8 only), y = W_down a^.
  * h_out[I] (may be NULL) receives a^, y[H] receives y. */
 void orc_expert_row(const orc_experts *W, int e, const double *xin, double *h_out, double *y)
@@ -297,7 +310,7 @@ void orc_expert_row(const orc_experts *W, int e, const double *xin, double *h_ou
             g += xq[h] * weight(W, W->w_gate, W->s_gate, e, j, h, I, H);
             u += xq[h] * weight(W, W->w_up, W->s_up, e, j, h, I, H);
         }
-        a[j] = g / (1.0 + exp(-g)) * u;
+        a[j] = gate_act(W->gate, g) * u;
     }
     if (W->act_fp8) quant_row(W, a, I, aq);
     else memcpy(aq, a, sizeof(double) * (size_t)I);

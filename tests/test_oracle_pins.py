@@ -325,6 +325,71 @@ def test_linear_in_down_projection_and_gate_is_silu_branch():
     assert not np.allclose(out4, 2 * out1)
 
 
+# ------------------------------------------------- GeGLU / ReGLU gates
+# Section "SonicMoE" of "Experts backends" lists gated activations silu, gelu
+# and relu (SwiGLU / GeGLU / ReGLU); gelu is read as the exact x * Phi(x).
+
+_GATES = {oracle.GATE_GELU: lambda g: torch.nn.functional.gelu(torch.from_numpy(g)).numpy(),
+          oracle.GATE_RELU: lambda g: np.maximum(g, 0.0)}
+
+
+@pytest.mark.parametrize("gate", [oracle.GATE_GELU, oracle.GATE_RELU])
+def test_single_expert_is_dense_glu_variant(gate):
+    # k = 1, E = 1: the layer is one dense gated MLP; torch's float64 gelu
+    # (exact form) and numpy's maximum are independent implementations
+    H, I, T = 32, 48, 12
+    wg, wu, wd = _rand_experts(1, H, I, 18)
+    x, wr = _tiny_router(T=T, H=H, E=1, seed=19)
+    ex = oracle.Experts(wg, wu, wd, gate=gate)
+    *_, out = oracle.forward(x, wr, None, ex, 1, oracle.SOFTMAX, True, 1.0)
+    xd = x.astype(np.float64)
+    g = xd @ wg[0].astype(np.float64).T
+    u = xd @ wu[0].astype(np.float64).T
+    ref = (_GATES[gate](g) * u) @ wd[0].astype(np.float64).T
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("gate", [oracle.GATE_SILU, oracle.GATE_GELU, oracle.GATE_RELU])
+def test_gate_odd_part_is_identity(gate):
+    # act(g) - act(-g) = g for silu, gelu (Phi(g) + Phi(-g) = 1) and relu, so
+    # negating W_gate changes the layer by exactly W_down (g * u): a closed
+    # form that catches a dropped factor or a wrong sign in any of the gates
+    H, I, E, T = 16, 24, 3, 10
+    wg, wu, wd = _rand_experts(E, H, I, 20)
+    x, wr = _tiny_router(T=T, H=H, E=E, seed=21)
+    ids, w, *_, out_p = oracle.forward(x, wr, None, oracle.Experts(wg, wu, wd, gate=gate), 2,
+                                       oracle.SOFTMAX, True, 1.0)
+    *_, out_n = oracle.forward(x, wr, None, oracle.Experts(-wg, wu, wd, gate=gate), 2,
+                               oracle.SOFTMAX, True, 1.0)
+    xd = x.astype(np.float64)
+    ref = np.zeros_like(out_p)
+    for t in range(T):
+        for i in range(2):
+            e = ids[t, i]
+            g = wg[e].astype(np.float64) @ xd[t]
+            u = wu[e].astype(np.float64) @ xd[t]
+            ref[t] += w[t, i] * (wd[e].astype(np.float64) @ (g * u))
+    assert np.allclose(out_p - out_n, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_gelu_gate_textbook_values():
+    # Phi(1) = 0.8413447460685429, Phi(-1) = 0.15865525393145707 and
+    # Phi(2) = 0.9772498680518208 (standard normal table): with H = I = 1 and
+    # all three weights 1, g = u = x and the layer returns gelu(x) * x =
+    # x^2 Phi(x)
+    x = np.array([[1.0], [-1.0], [0.0], [2.0]], dtype=np.float32)
+    one = np.ones((1, 1, 1), dtype=np.float32)
+    ex = oracle.Experts(one, one, one, gate=oracle.GATE_GELU)
+    h, y = ex.pairs(x, np.arange(4), [0, 0, 0, 0])
+    assert abs(y[0, 0] - 0.8413447460685429) < 1e-15
+    assert abs(y[1, 0] - 0.15865525393145707) < 1e-15
+    assert y[2, 0] == 0.0
+    assert abs(y[3, 0] - 4.0 * 0.9772498680518208) < 1e-14
+    exr = oracle.Experts(one, one, one, gate=oracle.GATE_RELU)
+    _, yr = exr.pairs(x, np.arange(4), [0, 0, 0, 0])
+    assert list(yr[:, 0]) == [1.0, 0.0, 0.0, 4.0]
+
+
 def _load_golden(name):
     vals = {}
     with open(os.path.join(GOLDEN, name)) as f:
