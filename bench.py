@@ -55,6 +55,8 @@ def parse():
                    choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8"])
     p.add_argument("--T", type=int, default=None)
     p.add_argument("--scale-fmt", default="f32", choices=["f32", "ue8m0"])
+    p.add_argument("--gate", default="silu", choices=["silu", "gelu", "relu"],
+                   help="gated activation of the experts (SwiGLU, GeGLU, ReGLU)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -100,6 +102,7 @@ def cpu_baseline(s, L, budget_s: float):
 
     hl = {k: (None if v is None else v.detach().cpu()) for k, v in L.items()}
     score = oracle.SOFTMAX if s.score == "softmax" else oracle.SIGMOID
+    gate = {"silu": oracle.GATE_SILU, "gelu": oracle.GATE_GELU, "relu": oracle.GATE_RELU}[s.gate]
     t0 = time.perf_counter()
     ids, w = oracle.route(hl["x"], hl["w_router"], hl["router_bias"], s.k, score, s.renormalize,
                           s.routed_scale)
@@ -107,9 +110,9 @@ def cpu_baseline(s, L, budget_s: float):
     if s.experts == "fp8":
         fmt = oracle.SCALE_UE8M0 if s.scale_fmt == "ue8m0" else oracle.SCALE_F32
         ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], hl["s_gate"], hl["s_up"],
-                            hl["s_down"], fmt, s.block, act_fp8=True)
+                            hl["s_down"], fmt, s.block, act_fp8=True, gate=gate)
     else:
-        ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"])
+        ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], gate=gate)
     rng = np.random.default_rng(0)
     order = rng.permutation(s.T)
     n, t_exp, done = 8, 0.0, 0
@@ -160,6 +163,8 @@ def main():
         over["T"] = args.T
     if args.config == "dsv3_fp8":
         over["scale_fmt"] = args.scale_fmt
+    if args.gate != "silu":
+        over["gate"] = args.gate
     s = synthetic.spec(args.config, **over)
     log("workload %s T=%d H=%d I=%d E=%d k=%d experts=%s" % (s.name, s.T, s.H, s.I, s.E, s.k, s.experts))
     t0 = time.perf_counter()
@@ -170,7 +175,8 @@ def main():
     layout = args.layout if s.experts != "f32" else "rowmajor"
     d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,
                       routed_scale=s.routed_scale, act_dtype=s.act, w_dtype=s.experts,
-                      w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none", layout=layout)
+                      w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none", layout=layout,
+                      gate=s.gate)
     if layout == "packed":
         # one-time model-load transform, outside the timed region
         wg, dn = moe.pack_experts(d, L["w_gate"], L["w_up"], L["w_down"], dev)
@@ -310,6 +316,7 @@ def main():
                    "experts": s.experts, "score": s.score, "renormalize": s.renormalize,
                    "routed_scale": s.routed_scale, "router_bias": s.bias, "weights": layout,
                    **({"scale_fmt": s.scale_fmt} if s.experts == "fp8" else {}),
+                   **({"gate": s.gate} if s.gate != "silu" else {}),
                    "layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,

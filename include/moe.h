@@ -91,6 +91,13 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } mo
  * is the packed down buffer.  Block scales keep their layout. */
 typedef enum { MOE_LAYOUT_ROWMAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
+/* Gated activation of the expert MLP, h = act(x . w_gate) * (x . w_up)
+ * ("Experts backends", section "SonicMoE": experts with a gated activation
+ * silu, gelu or relu, i.e. SwiGLU, GeGLU or ReGLU).  SILU: g / (1 + e^-g).
+ * GELU: the exact form g * Phi(g) = 0.5 g (1 + erf(g / sqrt 2)) (the page
+ * does not say which form).  RELU: max(g, 0).  Zero (the default) is SILU. */
+typedef enum { MOE_GATE_SILU = 0, MOE_GATE_GELU = 1, MOE_GATE_RELU = 2 } moe_gate_act;
+
 typedef enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1 } moe_pack_which;
 
 typedef enum {
@@ -116,7 +123,8 @@ typedef struct moe_desc {
     int32_t y_dtype;       /* expert-output rows y_sorted: MOE_DT_F32 or MOE_DT_BF16 */
     int32_t path;          /* moe_path */
     int32_t w_layout;      /* moe_layout of the expert weights */
-    int32_t reserved[2];   /* must be zero */
+    int32_t gate_act;      /* moe_gate_act of the expert MLPs */
+    int32_t reserved[1];   /* must be zero */
 } moe_desc;
 
 /* Supported combinations:

@@ -38,6 +38,7 @@ MOE_SCALE_NONE, MOE_SCALE_F32, MOE_SCALE_UE8M0 = range(3)
 MOE_ACT_NONE, MOE_ACT_DYNAMIC, MOE_ACT_STATIC = range(3)
 MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM = range(3)
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = range(2)
+MOE_GATE_SILU, MOE_GATE_GELU, MOE_GATE_RELU = range(3)
 MOE_PACK_GATE_UP, MOE_PACK_DOWN = range(2)
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GATE_UP, MOE_OP_DOWN, MOE_OP_COMBINE,
  MOE_OP_FORWARD) = range(6)
@@ -53,7 +54,7 @@ class MoeDesc(ctypes.Structure):
                 ("w_scale_fmt", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("act_scheme", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
                 ("path", ctypes.c_int32), ("w_layout", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("gate_act", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class MoeError(RuntimeError):
@@ -106,7 +107,7 @@ def library():
 
 def make_desc(T, H, I, E, k, *, score="softmax", renormalize=False, routed_scale=1.0,
               act_dtype="bf16", w_dtype="bf16", w_scale_fmt="none", block=None,
-              act_scheme=None, y_dtype=None, path="auto", layout="rowmajor") -> MoeDesc:
+              act_scheme=None, y_dtype=None, path="auto", layout="rowmajor", gate="silu") -> MoeDesc:
     dt = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "fp8": MOE_DT_FP8_E4M3}
     d = MoeDesc()
     d.T, d.H, d.I, d.E, d.k = int(T), int(H), int(I), int(E), int(k)
@@ -126,6 +127,7 @@ def make_desc(T, H, I, E, k, *, score="softmax", renormalize=False, routed_scale
     d.y_dtype = dt[y_dtype]
     d.path = {"auto": MOE_PATH_AUTO, "grouped": MOE_PATH_GROUPED, "stream": MOE_PATH_STREAM}[path]
     d.w_layout = {"rowmajor": MOE_LAYOUT_ROWMAJOR, "packed": MOE_LAYOUT_PACKED}[layout]
+    d.gate_act = {"silu": MOE_GATE_SILU, "gelu": MOE_GATE_GELU, "relu": MOE_GATE_RELU}[gate]
     return d
 
 

@@ -69,6 +69,8 @@ moe_status validate(const moe_desc* d) {
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_STREAM) return fail(MOE_EINVAL, "path = %d", d->path);
   for (int r : d->reserved)
     if (r != 0) return fail(MOE_EINVAL, "reserved fields must be zero");
+  if (d->gate_act < MOE_GATE_SILU || d->gate_act > MOE_GATE_RELU)
+    return fail(MOE_EINVAL, "gate_act = %d is not a moe_gate_act", d->gate_act);
   if (d->w_layout != MOE_LAYOUT_ROWMAJOR && d->w_layout != MOE_LAYOUT_PACKED)
     return fail(MOE_EINVAL, "w_layout = %d", d->w_layout);
   if (d->w_layout == MOE_LAYOUT_PACKED && d->w_dtype == MOE_DT_F32)
@@ -355,6 +357,7 @@ GemmArgs gemm_common(const moe_desc* d) {
   a.E = d->E;
   a.P = pairs(d);
   a.scale_ue8m0 = d->w_scale_fmt == MOE_SCALE_UE8M0;
+  a.gate_act = d->gate_act;
   return a;
 }
 

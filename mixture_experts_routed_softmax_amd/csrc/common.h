@@ -52,6 +52,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // silu(g) = g * sigmoid(g); v_rcp_f32 (1 ulp) instead of an IEEE division
 __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// gate activation of the gated MLP (moe_gate_act: 0 silu, 1 gelu, 2 relu);
+// gelu is the exact form 0.5 g (1 + erf(g / sqrt 2)).  `act` is uniform.
+__device__ __forceinline__ float gate_fn(float g, int act) {
+  if (act == 1) return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+  if (act == 2) return fmaxf(g, 0.0f);
+  return silu(g);
+}
+
 // value of an E8M0 scale byte: 2^(b-127)
 __device__ __forceinline__ float e8m0_to_f32(uint8_t b) { return __builtin_ldexpf(1.0f, (int)b - 127); }
 

@@ -5,7 +5,8 @@
 // up projection, SwiGLU, down projection) as one grouped GEMM over the
 // expert-sorted rows (rows grouped_mm / deepgemm).
 //
-//   gate/up : h[r, j] = silu(x_r . w_gate[e, j]) * (x_r . w_up[e, j])
+//   gate/up : h[r, j] = act(x_r . w_gate[e, j]) * (x_r . w_up[e, j]),
+//             act = silu, gelu or relu (GemmArgs.gate_act)
 //   down    : y[r, o] = h_r . w_down[e, o]
 //
 // Tile = 512 weight rows x 128 token rows, K step 32, 4 waves stacked along
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
           uint16_t v[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            v[c] = f32_to_bf16_bits(silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c]);
+            v[c] = f32_to_bf16_bits(gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c]);
           i32x2 pk = {(int)(v[0] | ((uint32_t)v[1] << 16)), (int)(v[2] | ((uint32_t)v[3] << 16))};
           *(i32x2*)(h + ch) = pk;
         }

@@ -1,7 +1,7 @@
 // fp32 expert MLPs (small fp32 layers): one thread per (sorted row, output
 // channel), fp32 FMA over the reduction.  Same arithmetic as the grouped
 // GEMMs ("Experts backends", backend table, row deepgemm_megamoe: up
-// projection with SwiGLU gate, down projection), without tiling: these layers
+// projection with the gated activation, down projection), without tiling: these layers
 // are tiny and exist for exact-precision parity.
 #include "common.h"
 #include "kernels.h"
@@ -35,7 +35,11 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(GemmArgs a) {
     g = __builtin_fmaf(x[h], wg[h], g);
     u = __builtin_fmaf(x[h], wu[h], u);
   }
-  ((float*)a.out)[(int64_t)r * a.N + j] = g / (1.0f + expf(-g)) * u;
+  float act;
+  if (a.gate_act == 1) act = 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));   // exact gelu
+  else if (a.gate_act == 2) act = fmaxf(g, 0.0f);                                   // relu
+  else act = g / (1.0f + expf(-g));                                                 // silu
+  ((float*)a.out)[(int64_t)r * a.N + j] = act * u;
 }
 
 __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs a) {

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float v = silu(acc[i][tj][r]) * acc[2 + i][tj][r];
+          const float v = gate_fn(acc[i][tj][r], a.gate_act) * acc[2 + i][tj][r];
           hv[tj][i][r] = v;
           m = fmaxf(m, fabsf(v));
         }

@@ -6,7 +6,8 @@
 // deepgemm); FP8 experts carry 128 x 128 block scales (float32 or UE8M0) and
 // dynamic per-row activation scales (section "FP8 and FP4 quantized experts").
 //
-//   gate/up : h[r, j] = silu(x_r . w_gate[e, j]) * (x_r . w_up[e, j])
+//   gate/up : h[r, j] = act(x_r . w_gate[e, j]) * (x_r . w_up[e, j]),
+//             act = silu, gelu or relu (GemmArgs.gate_act)
 //   down    : y[r, o] = h_r . w_down[e, o]
 //
 // The weights are in the packed layout written by pack.hip: for every
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
         float m = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          hv[j][r] = silu(acc[0][j][r]) * acc[1][j][r];
+          hv[j][r] = gate_fn(acc[0][j][r], a.gate_act) * acc[1][j][r];
           m = fmaxf(m, fabsf(hv[j][r]));
         }
         m = fmaxf(m, __shfl_xor(m, 32));
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
           if (ch >= N) continue;
           float v[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c];
+          for (int c = 0; c < 4; ++c) v[c] = gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c];
           *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
         }
       }

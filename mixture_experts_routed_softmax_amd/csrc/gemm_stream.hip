@@ -7,7 +7,8 @@
 // weights from HBM; this kernel reads every weight byte exactly once, spread
 // over all compute units, and multiplies it against the (L2-resident) token
 // rows of its expert:
-//   gate/up : h[r, j] = silu(x_r . w_gate[e, j]) * (x_r . w_up[e, j])
+//   gate/up : h[r, j] = act(x_r . w_gate[e, j]) * (x_r . w_up[e, j]),
+//             act = silu, gelu or relu (GemmArgs.gate_act)
 //   down    : y[r, o] = h_r . w_down[e, o]
 //
 // Work item = (touched expert, packed 256-row tile); 4 waves, each owning 64
@@ -71,7 +72,7 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
         float m = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          hv[j][r] = silu(acc[0][j][r]) * acc[1][j][r];
+          hv[j][r] = gate_fn(acc[0][j][r], a.gate_act) * acc[1][j][r];
           m = fmaxf(m, fabsf(hv[j][r]));
         }
         m = fmaxf(m, __shfl_xor(m, 32));
@@ -105,7 +106,7 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
           if (ch >= N) continue;
           float v[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = silu(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c];
+          for (int c = 0; c < 4; ++c) v[c] = gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c];
           *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
         }
       }
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
         const int o = row * 256 + (c >> 5) * 64 + (c & 31);
         float g, u;
         total2(o, o + 32, g, u);
-        hv = silu(g) * u;
+        hv = gate_fn(g, a.gate_act) * u;
       }
       const int ch = it.ntile * 128 + c;
       if constexpr (kFp8) {

@@ -77,6 +77,7 @@ struct GemmArgs {
   int64_t P;
   int wtiles;               // packed weights: row tiles per expert
   float* partial;           // weight streaming: split-K partial tiles
+  int gate_act;             // moe_gate_act of the gate/up epilogue
 };
 
 // tile geometry of the grouped GEMMs

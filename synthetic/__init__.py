@@ -65,6 +65,7 @@ class LayerSpec:
     bias: str           # "none" | "zero" | "zipf"
     scale_fmt: str = "none"   # fp8 weight scales: "f32" | "ue8m0"
     block: int = 128
+    gate: str = "silu"        # gated activation of the expert MLPs: "silu" | "gelu" | "relu"
 
     @property
     def P(self) -> int:

@@ -26,7 +26,7 @@ def desc_for(s: synthetic.LayerSpec, T: int | None = None, path: str = "auto", y
                          renormalize=s.renormalize, routed_scale=s.routed_scale,
                          act_dtype=s.act, w_dtype=s.experts,
                          w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none",
-                         y_dtype=y_dtype, path=path, layout=layout)
+                         y_dtype=y_dtype, path=path, layout=layout, gate=s.gate)
 
 
 def expert_weights(d, L: dict):
@@ -46,11 +46,12 @@ def host(layer: dict) -> dict:
 
 
 def oracle_experts(s, hl: dict) -> oracle.Experts:
+    gate = {"silu": oracle.GATE_SILU, "gelu": oracle.GATE_GELU, "relu": oracle.GATE_RELU}[s.gate]
     if s.experts == "fp8":
         fmt = oracle.SCALE_UE8M0 if s.scale_fmt == "ue8m0" else oracle.SCALE_F32
         return oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], hl["s_gate"], hl["s_up"],
-                              hl["s_down"], fmt, s.block, act_fp8=True)
-    return oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"])
+                              hl["s_down"], fmt, s.block, act_fp8=True, gate=gate)
+    return oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], gate=gate)
 
 
 def oracle_route(s, hl):

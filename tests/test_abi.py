@@ -80,6 +80,8 @@ def test_status_strings():
     (dict(w_scale_fmt=moe.MOE_SCALE_F32), moe.MOE_EINVAL),   # scales on bf16 experts
     (dict(act_dtype=moe.MOE_DT_F32), moe.MOE_EUNSUPPORTED),  # f32 x with bf16 experts
     (dict(reserved=1), moe.MOE_EINVAL),
+    (dict(gate_act=3), moe.MOE_EINVAL),
+    (dict(gate_act=-1), moe.MOE_EINVAL),
     (dict(k=33, E=64), moe.MOE_EUNSUPPORTED),
 ])
 def test_validation_rejects(bad, status):

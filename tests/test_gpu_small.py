@@ -301,3 +301,28 @@ def test_forward_replays_as_graph():
         step()   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
+
+
+# GeGLU / ReGLU experts ("Experts backends", section "SonicMoE": gated
+# activation silu, gelu or relu) on every expert-GEMM kernel family: fp32,
+# bf16 and fp8 grouped GEMMs (row-major and packed weights) and the
+# weight-streaming GEMMs with split-K reduction.
+GATE_CASES = [(g, name, layout, path) for g in ("gelu", "relu") for name, layout, path in [
+    ("tiny", "rowmajor", "grouped"), ("bf16_softmax", "rowmajor", "grouped"),
+    ("bf16_softmax", "packed", "grouped"), ("fp8_f32", "rowmajor", "grouped"),
+    ("fp8_ue8m0", "packed", "grouped"), ("bf16_decode_split_hot", "packed", "stream"),
+    ("fp8_decode_split", "packed", "stream")]]
+
+
+@pytest.mark.parametrize("gate,name,layout,path", GATE_CASES)
+def test_gated_activation_variants(gate, name, layout, path):
+    import dataclasses
+    s = dataclasses.replace(SMALL[name] if name in SMALL else STREAM[name], gate=gate)
+    L, hl = _layer(s, seed=16)
+    ids_o, w_o = oracle_route(s, hl)
+    out, ids, w, counts = run_forward(s, L, path=path, layout=layout)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    out_o = oracle_experts(s, hl).combine(hl["x"], ids_o, w_o)
+    err = row_rel_err(out.cpu().float().numpy(), out_o)
+    print("%s %s %s %s: max row rel err %.3e" % (gate, name, layout, path, err))
+    assert err <= tol_of(s)
