@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, E2M1 = 0, 1, 2, 3
 SOFTMAX, SIGMOID = 0, 1
 SCALE_NONE, SCALE_F32, SCALE_UE8M0 = 0, 1, 2
 GATE_SILU, GATE_GELU, GATE_RELU = 0, 1, 2    # SwiGLU / GeGLU / ReGLU
@@ -61,6 +61,8 @@ def lib():
         L.orc_bf16_to_f64.restype = dbl
         L.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_to_f64.restype = dbl
+        L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_f64.restype = dbl
         L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
         L.orc_e8m0_to_f64.restype = dbl
         L.orc_e4m3_encode.argtypes = [dbl]
@@ -132,6 +134,10 @@ def bf16_to_f64(bits: int) -> float:
 
 def e4m3_to_f64(code: int) -> float:
     return lib().orc_e4m3_to_f64(code)
+
+
+def e2m1_to_f64(code: int) -> float:
+    return lib().orc_e2m1_to_f64(code)
 
 
 def e8m0_to_f64(b: int) -> float:
@@ -216,6 +222,7 @@ class Experts:
     block: int = 128
     act_fp8: bool = False
     gate: int = 0            # GATE_SILU, GATE_GELU or GATE_RELU
+    fp4: bool = False        # uint8 weights hold two E2M1 codes per byte along K
 
     def __post_init__(self):
         self._arrs = []
@@ -226,13 +233,18 @@ class Experts:
             raise ValueError("gate/up/down must share one format")
         E, I, H = g.shape
         sg = su = sd = None
-        if gf == E4M3:
+        if self.fp4:
+            if gf != E4M3 or self.scale_fmt != SCALE_UE8M0:
+                raise ValueError("fp4 experts are uint8 code pairs with UE8M0 scales")
+            gf = E2M1
+            H *= 2
+        if gf in (E4M3, E2M1):
             sg = _as_host_scale(self.s_gate, self.scale_fmt)
             su = _as_host_scale(self.s_up, self.scale_fmt)
             sd = _as_host_scale(self.s_down, self.scale_fmt)
         self._arrs = [g, u, d, sg, su, sd]
         self.E, self.I, self.H = E, I, H
-        self._st = _Experts(H, I, E, gf, self.scale_fmt if gf == E4M3 else SCALE_NONE,
+        self._st = _Experts(H, I, E, gf, self.scale_fmt if gf in (E4M3, E2M1) else SCALE_NONE,
                             self.block, int(bool(self.act_fp8)), int(self.gate),
                             g.ctypes.data, u.ctypes.data, d.ctypes.data,
                             None if sg is None else sg.ctypes.data,

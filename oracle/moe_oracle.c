@@ -17,9 +17,9 @@
  *     a gated MLP -- up projection, gated activation, down projection; the
  *     gate is silu, gelu or relu (SwiGLU / GeGLU / ReGLU, section "SonicMoE");
  *   - paragraph under the backend table and section "FP8 and FP4 quantized
- *     experts": FP8 experts carry float32 or UE8M0 block scales, and activations
- *     are quantized with dynamic per-row scales (static per-tensor scales are
- *     rejected).
+ *     experts": FP8 experts carry float32 or UE8M0 block scales, FP4 experts
+ *     are int8-packed with UE8M0 scales, and activations are quantized with
+ *     dynamic per-row scales (static per-tensor scales are rejected).
  *
  * Readings where the page is silent (the page gives no formula for the router,
  * no shapes and no block size):
@@ -39,6 +39,9 @@
  *     scale s = fl32(amax / 448), code = RNE_e4m3(fl32(v / s)) saturated at
  *     448, amax = 0 -> all codes 0.  The intermediate a (the SwiGLU output) is
  *     quantized the same way before the down projection.
+ *   - FP4: OCP e2m1 codes, two per byte along K (even K in the low nibble),
+ *     one UE8M0 scale per row per 32 consecutive K (the OCP MX block; the page
+ *     gives no FP4 block size); activations as for FP8 (e4m3, per row per 128).
  *
  * Pins: every function here is checked by the CPU tests against closed forms,
  * library routines on special cases, brute force on tiny inputs and a worked
@@ -53,7 +56,9 @@
 #endif
 
 /* element formats understood by the oracle */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_E2M1 = 3 };
+/* FP4 weight scale block: one UE8M0 scale per row per 32 consecutive K */
+#define ORC_FP4_BLOCK 32
 /* score functions */
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };
 /* fp8 weight-scale formats */
@@ -87,6 +92,18 @@ double orc_e4m3_to_f64(uint8_t code)
         v = ldexp((double)man / 8.0, -6);
     else
         v = ldexp(1.0 + (double)man / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* OCP 4-bit float E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit;
+ * exponent field 0 holds the subnormal m * 0.5; no NaN or infinity.  Values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives.  `code` is one nibble. */
+double orc_e2m1_to_f64(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int ex = (code >> 1) & 3;
+    int man = code & 1;
+    double v = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
     return sign ? -v : v;
 }
 
@@ -247,7 +264,7 @@ void orc_permute(int64_t T, int k, int E, const int32_t *ids,
 
 typedef struct {
     int32_t H, I, E;
-    int32_t wdt;        /* ORC_F32, ORC_BF16 or ORC_E4M3 for all three matrices */
+    int32_t wdt;        /* ORC_F32, ORC_BF16, ORC_E4M3 or ORC_E2M1 for all three matrices */
     int32_t scale_fmt;  /* ORC_SCALE_*; used only with ORC_E4M3 */
     int32_t block;      /* weight block edge and activation group size (fp8) */
     int32_t act_fp8;    /* quantize x and a per row per `block` channels */
@@ -269,10 +286,20 @@ static double block_scale(const orc_experts *W, const void *s, int e, int r, int
     return 1.0;
 }
 
-/* one weight element of matrix m [E, rows, cols] as an exact fp64 value */
+/* one weight element of matrix m [E, rows, cols] as an exact fp64 value.
+ * E2M1 ("int8-packed" FP4, paragraph under the backend table): two codes per
+ * byte along cols, the even column in the low nibble, times the UE8M0 scale of
+ * its (row, 32-column) block, s [E, rows, cols / 32]. */
 static double weight(const orc_experts *W, const void *m, const void *s, int e, int r, int c,
                      int rows, int cols)
 {
+    if (W->wdt == ORC_E2M1) {
+        int64_t idx = ((int64_t)e * rows + r) * cols + c;
+        uint8_t byte = ((const uint8_t *)m)[idx / 2];
+        double v = orc_e2m1_to_f64((c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15));
+        int64_t sidx = ((int64_t)e * rows + r) * (cols / ORC_FP4_BLOCK) + c / ORC_FP4_BLOCK;
+        return v * orc_e8m0_to_f64(((const uint8_t *)s)[sidx]);
+    }
     double v = decode_elem(m, W->wdt, ((int64_t)e * rows + r) * cols + c);
     if (W->wdt == ORC_E4M3) v *= block_scale(W, s, e, r, c, rows, cols);
     return v;

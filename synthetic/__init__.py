@@ -58,7 +58,7 @@ class LayerSpec:
     E: int
     k: int
     act: str            # "f32" | "bf16": x, W_r and the layer output
-    experts: str        # "f32" | "bf16" | "fp8"
+    experts: str        # "f32" | "bf16" | "fp8" | "fp4"
     score: str          # "softmax" | "sigmoid"
     renormalize: bool
     routed_scale: float
@@ -82,6 +82,10 @@ _BASE = {
                            True, 2.5, "zipf"),
     "dsv3_fp8": LayerSpec("dsv3_fp8", 8192, 7168, 2048, 256, 8, "bf16", "fp8", "sigmoid",
                           True, 2.5, "zipf", "f32"),
+    # the DeepSeek-like layer with int8-packed FP4 experts (UE8M0 scales per
+    # row per 32 K; activations fp8 per row per 128)
+    "dsv3_fp4": LayerSpec("dsv3_fp4", 8192, 7168, 2048, 256, 8, "bf16", "fp4", "sigmoid",
+                          True, 2.5, "zipf", "ue8m0"),
 }
 
 # token counts each workload is exercised at
@@ -151,6 +155,8 @@ def make_layer(s: LayerSpec, seed: int = 0, device="cpu") -> dict:
 
     if s.experts == "fp8":
         out.update(_fp8_experts(s, seed, device))
+    elif s.experts == "fp4":
+        out.update(_fp4_experts(s, seed, device))
     else:
         out.update(_dense_experts(s, seed, device))
     return out
@@ -209,6 +215,33 @@ def _fp8_experts(s: LayerSpec, seed: int, device) -> dict:
         else:
             u = torch.rand(shape, generator=g, device=device, dtype=torch.float32) - 0.5
             res[sname] = (0.02 / 112.0) * torch.exp2(u)
+    return res
+
+
+_E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _fp4_experts(s: LayerSpec, seed: int, device) -> dict:
+    """E2M1 code pairs [E, rows, cols/2] (even column in the low nibble) and
+    UE8M0 scale bytes [E, rows, cols/32]; codes follow N(0, 2) snapped to the
+    nearest E2M1 value, scales 2^-8 .. 2^-6 (weights of std about 0.02)."""
+    mags = torch.tensor(_E2M1_VALUES, device=device)
+    res = {}
+    for name, (rows, cols) in (("w_gate", (s.I, s.H)), ("w_up", (s.I, s.H)),
+                               ("w_down", (s.H, s.I))):
+        codes = torch.empty(s.E, rows, cols // 2, dtype=torch.uint8, device=device)
+        for e in range(s.E):
+            g = _gen(device, seed, s.name, name, e)
+            v = torch.randn(rows, cols, generator=g, device=device) * 2.0
+            c = (v.abs().unsqueeze(-1) - mags).abs().argmin(-1)          # nearest magnitude
+            c = c | ((v < 0) & (c > 0)).to(torch.int64) << 3            # sign (no -0)
+            c = c.to(torch.uint8).view(rows, cols // 2, 2)
+            codes[e] = c[..., 0] | (c[..., 1] << 4)
+        res[name] = codes
+        sname = "s_" + name[2:]
+        g = _gen(device, seed, s.name, sname)
+        res[sname] = torch.randint(119, 122, (s.E, rows, cols // 32), generator=g, device=device,
+                                   dtype=torch.int64).to(torch.uint8)
     return res
 
 

@@ -34,6 +34,55 @@ def test_e4m3_decode_exhaustive_vs_torch():
     assert oracle.e4m3_to_f64(0x01) == 2.0 ** -9
 
 
+# OCP Microscaling (MX) formats, FP4 E2M1 element table: magnitudes of the
+# eight codes 0..7 (the definition of the format; code + 8 negates)
+_E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_exhaustive():
+    for c in range(16):
+        v = _E2M1_TABLE[c & 7] * (-1.0 if c & 8 else 1.0)
+        got = oracle.e2m1_to_f64(c)
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), (c, got, v)
+    # every E2M1 value is an E4M3 value (torch's conversion is exact for them)
+    for v in _E2M1_TABLE:
+        assert torch.tensor(v).to(torch.float8_e4m3fn).float().item() == v
+
+
+def _fp4_dense(codes, scales):
+    """float64 weights from E2M1 code pairs [E, R, C/2] and UE8M0 bytes [E, R, C/32]."""
+    lo = codes & 15
+    hi = codes >> 4
+    c = np.stack([lo, hi], axis=-1).reshape(codes.shape[0], codes.shape[1], -1)
+    tab = np.array(_E2M1_TABLE + [-v for v in _E2M1_TABLE])
+    s = np.repeat(np.exp2(scales.astype(np.float64) - 127.0), 32, axis=2)
+    return tab[c] * s
+
+
+def test_fp4_experts_equal_dense_weights():
+    # int8-packed E2M1 with one UE8M0 scale per (row, 32 K) equals the dense
+    # fp64 weights built from the format table: pins the nibble order, the
+    # code table and the scale indexing of both matrix shapes
+    E, H, I = 3, 64, 96
+    rng = np.random.default_rng(30)
+    cg = rng.integers(0, 256, (E, I, H // 2), dtype=np.uint8)
+    cu = rng.integers(0, 256, (E, I, H // 2), dtype=np.uint8)
+    cd = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    sg = rng.integers(118, 126, (E, I, H // 32), dtype=np.uint8)
+    su = rng.integers(118, 126, (E, I, H // 32), dtype=np.uint8)
+    sd = rng.integers(118, 126, (E, H, I // 32), dtype=np.uint8)
+    fp4 = oracle.Experts(cg, cu, cd, sg, su, sd, oracle.SCALE_UE8M0, fp4=True)
+    dg, du, dd = _fp4_dense(cg, sg), _fp4_dense(cu, su), _fp4_dense(cd, sd)
+    assert np.array_equal(dg.astype(np.float32), dg) and np.array_equal(dd.astype(np.float32), dd)
+    dense = oracle.Experts(dg.astype(np.float32), du.astype(np.float32), dd.astype(np.float32))
+    x = rng.normal(0, 1, (5, H)).astype(np.float32)
+    tok = np.array([0, 1, 2, 3, 4, 0])
+    ex = np.array([0, 1, 2, 1, 0, 2])
+    h1, y1 = fp4.pairs(x, tok, ex)
+    h2, y2 = dense.pairs(x, tok, ex)
+    assert np.array_equal(h1, h2) and np.array_equal(y1, y2)
+
+
 def test_e8m0_decode_exhaustive_vs_torch():
     b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
     ref = b.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
