@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 5000.0, "f32": 157.3}   # fp4 experts: fp8 x fp4 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/s; % MFMA peak (prefill), % HBM BW (decode)"
 
@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="qwen_prefill",
-                   choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8"])
+                   choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8", "dsv3_fp4"])
     p.add_argument("--T", type=int, default=None)
     p.add_argument("--scale-fmt", default="f32", choices=["f32", "ue8m0"])
     p.add_argument("--gate", default="silu", choices=["silu", "gelu", "relu"],
@@ -107,10 +107,10 @@ def cpu_baseline(s, L, budget_s: float):
     ids, w = oracle.route(hl["x"], hl["w_router"], hl["router_bias"], s.k, score, s.renormalize,
                           s.routed_scale)
     t_route = time.perf_counter() - t0
-    if s.experts == "fp8":
+    if s.experts in ("fp8", "fp4"):
         fmt = oracle.SCALE_UE8M0 if s.scale_fmt == "ue8m0" else oracle.SCALE_F32
         ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], hl["s_gate"], hl["s_up"],
-                            hl["s_down"], fmt, s.block, act_fp8=True, gate=gate)
+                            hl["s_down"], fmt, s.block, act_fp8=True, gate=gate, fp4=s.experts == "fp4")
     else:
         ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], gate=gate)
     rng = np.random.default_rng(0)
@@ -175,7 +175,7 @@ def main():
     layout = args.layout if s.experts != "f32" else "rowmajor"
     d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,
                       routed_scale=s.routed_scale, act_dtype=s.act, w_dtype=s.experts,
-                      w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none", layout=layout,
+                      w_scale_fmt=s.scale_fmt if s.experts in ("fp8", "fp4") else "none", layout=layout,
                       gate=s.gate)
     if layout == "packed":
         # one-time model-load transform, outside the timed region
@@ -271,7 +271,9 @@ def main():
     P = s.T * s.k
     cnt = counts.cpu()
     touched = int((cnt > 0).sum())
-    wbytes_per_expert = 3 * s.H * s.I * (1 if s.experts == "fp8" else (4 if s.experts == "f32" else 2))
+    wbytes_per_expert = 3 * s.H * s.I * {"fp4": 0.5, "fp8": 1, "bf16": 2, "f32": 4}[s.experts]
+    if s.experts == "fp4":
+        wbytes_per_expert += 3 * s.H * s.I // 32    # one UE8M0 scale byte per 32 weights
     if decode:
         # HBM roofline of the whole step: weights of the touched experts only
         alg_bytes = touched * wbytes_per_expert
@@ -311,11 +313,12 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[s.experts], "data": "synthetic",
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3", "fp4": "fp4_e2m1"}[s.experts],
+        "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
                    "experts": s.experts, "score": s.score, "renormalize": s.renormalize,
                    "routed_scale": s.routed_scale, "router_bias": s.bias, "weights": layout,
-                   **({"scale_fmt": s.scale_fmt} if s.experts == "fp8" else {}),
+                   **({"scale_fmt": s.scale_fmt} if s.experts in ("fp8", "fp4") else {}),
                    **({"gate": s.gate} if s.gate != "silu" else {}),
                    "layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1)},
         "roofline": roof,

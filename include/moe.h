@@ -52,7 +52,14 @@ typedef enum {
     MOE_EHIP = 4             /* the HIP runtime reported an error at launch */
 } moe_status;
 
-typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2 } moe_dtype;
+/* FP4_E2M1: int8-packed FP4 expert weights (the paragraph under the backend
+ * table and section "FP8 and FP4 quantized experts": FP4 experts packed in
+ * int8 with UE8M0 scales): OCP e2m1 codes, two per byte along K with the even
+ * K index in the low nibble, so w_gate, w_up are [E,I,H/2] bytes and w_down
+ * [E,H,I/2]; one UE8M0 scale per row per 32 consecutive K (the OCP MX block;
+ * the page gives no FP4 block size): w_gate_scales, w_up_scales [E,I,H/32],
+ * w_down_scales [E,H,I/32] bytes.  Weights only (activations are e4m3). */
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8_E4M3 = 2, MOE_DT_FP4_E2M1 = 3 } moe_dtype;
 
 /* Router score, applied to key[e] = x . w_router[e] + router_bias[e].
  * Experts are selected by descending key, ties to the lowest expert index. */
@@ -116,10 +123,11 @@ typedef struct moe_desc {
     int32_t renormalize;   /* 1: selected scores are divided by their sum */
     float routed_scale;    /* multiplies the final routing weights */
     int32_t act_dtype;     /* MOE_DT_F32 or MOE_DT_BF16: x, w_router and out */
-    int32_t w_dtype;       /* expert weights: MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3 */
-    int32_t w_scale_fmt;   /* MOE_SCALE_NONE, or F32 / UE8M0 with FP8 weights */
-    int32_t block;         /* FP8 weight block edge and activation group: 128 (else 0) */
-    int32_t act_scheme;    /* MOE_ACT_NONE, or MOE_ACT_DYNAMIC with FP8 weights */
+    int32_t w_dtype;       /* expert weights: MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3, MOE_DT_FP4_E2M1 */
+    int32_t w_scale_fmt;   /* MOE_SCALE_NONE, or F32 / UE8M0 with FP8 weights, UE8M0 with FP4 */
+    int32_t block;         /* FP8 weight block edge and activation group: 128 (FP4: the
+                              activation group, 128); else 0 */
+    int32_t act_scheme;    /* MOE_ACT_NONE, or MOE_ACT_DYNAMIC with FP8 / FP4 weights */
     int32_t y_dtype;       /* expert-output rows y_sorted: MOE_DT_F32 or MOE_DT_BF16 */
     int32_t path;          /* moe_path */
     int32_t w_layout;      /* moe_layout of the expert weights */
@@ -134,8 +142,12 @@ typedef struct moe_desc {
  *            (x and h are quantized to e4m3 per row per 128 channels with
  *             fp32 scales amax/448; fp8 MFMA, fp32 accumulate, block scales
  *             applied per 128-deep K chunk in fp32)
- * Intermediate h [P,I] is in the expert weight format (bf16/f32, or e4m3 codes
- * plus fp32 scales [P,I/128]). */
+ *   act BF16 + weights FP4_E2M1, scales UE8M0, block 128, act DYNAMIC, PACKED
+ *            layout only (x and h as for FP8; fp8 x fp4 MFMA with the weights'
+ *            per-32 scales applied by the MFMA, activation scales per 128-deep
+ *            K chunk in fp32; MOE_EUNSUPPORTED for row-major weights)
+ * Intermediate h [P,I] is in the expert weight format (bf16/f32), or e4m3
+ * codes plus fp32 scales [P,I/128] for FP8 and FP4 experts. */
 
 /* ------------------------------------------------------------------------ */
 

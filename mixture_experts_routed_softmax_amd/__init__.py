@@ -32,7 +32,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # ---- enums (values of include/moe.h)
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
-MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3 = range(3)
+MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3, MOE_DT_FP4_E2M1 = range(4)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 MOE_SCALE_NONE, MOE_SCALE_F32, MOE_SCALE_UE8M0 = range(3)
 MOE_ACT_NONE, MOE_ACT_DYNAMIC, MOE_ACT_STATIC = range(3)
@@ -108,7 +108,7 @@ def library():
 def make_desc(T, H, I, E, k, *, score="softmax", renormalize=False, routed_scale=1.0,
               act_dtype="bf16", w_dtype="bf16", w_scale_fmt="none", block=None,
               act_scheme=None, y_dtype=None, path="auto", layout="rowmajor", gate="silu") -> MoeDesc:
-    dt = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "fp8": MOE_DT_FP8_E4M3}
+    dt = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "fp8": MOE_DT_FP8_E4M3, "fp4": MOE_DT_FP4_E2M1}
     d = MoeDesc()
     d.T, d.H, d.I, d.E, d.k = int(T), int(H), int(I), int(E), int(k)
     d.score = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score]
@@ -117,7 +117,7 @@ def make_desc(T, H, I, E, k, *, score="softmax", renormalize=False, routed_scale
     d.act_dtype = dt[act_dtype]
     d.w_dtype = dt[w_dtype]
     d.w_scale_fmt = {"none": MOE_SCALE_NONE, "f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0}[w_scale_fmt]
-    fp8 = w_dtype == "fp8"
+    fp8 = w_dtype in ("fp8", "fp4")
     d.block = int(block if block is not None else (128 if fp8 else 0))
     if act_scheme is None:
         act_scheme = "dynamic" if fp8 else "none"

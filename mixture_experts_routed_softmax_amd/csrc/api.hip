@@ -45,8 +45,16 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int64_t pairs(const moe_desc* d) { return d->T * (int64_t)d->k; }
 
 size_t elt_bytes(int dt) { return dt == MOE_DT_F32 ? 4 : dt == MOE_DT_BF16 ? 2 : 1; }
+// bytes of one weight row of K values (fp4: two codes per byte)
+int64_t w_row_bytes(int dt, int64_t K) { return dt == MOE_DT_FP4_E2M1 ? K / 2 : K * (int64_t)elt_bytes(dt); }
 
-bool is_fp8(const moe_desc* d) { return d->w_dtype == MOE_DT_FP8_E4M3; }
+// quantized experts (fp8 or fp4 weights): activations and h are e4m3 codes
+// with per-row per-128 fp32 scales
+bool is_fp8(const moe_desc* d) { return d->w_dtype == MOE_DT_FP8_E4M3 || d->w_dtype == MOE_DT_FP4_E2M1; }
+// weight format code of the streaming / packed kernels: 0 bf16, 1 fp8, 2 fp4
+int wfmt(const moe_desc* d) {
+  return d->w_dtype == MOE_DT_FP4_E2M1 ? 2 : (d->w_dtype == MOE_DT_FP8_E4M3 ? 1 : 0);
+}
 
 moe_status validate(const moe_desc* d) {
   if (!d) return fail(MOE_EINVAL, "desc is NULL");
@@ -62,7 +70,8 @@ moe_status validate(const moe_desc* d) {
   if (!std::isfinite(d->routed_scale)) return fail(MOE_EINVAL, "routed_scale is not finite");
   if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16)
     return fail(MOE_EINVAL, "act_dtype = %d", d->act_dtype);
-  if (d->w_dtype != MOE_DT_F32 && d->w_dtype != MOE_DT_BF16 && d->w_dtype != MOE_DT_FP8_E4M3)
+  if (d->w_dtype != MOE_DT_F32 && d->w_dtype != MOE_DT_BF16 && d->w_dtype != MOE_DT_FP8_E4M3 &&
+      d->w_dtype != MOE_DT_FP4_E2M1)
     return fail(MOE_EINVAL, "w_dtype = %d", d->w_dtype);
   if (d->y_dtype != MOE_DT_F32 && d->y_dtype != MOE_DT_BF16)
     return fail(MOE_EINVAL, "y_dtype = %d", d->y_dtype);
@@ -82,7 +91,12 @@ moe_status validate(const moe_desc* d) {
   if (d->act_scheme < MOE_ACT_NONE || d->act_scheme > MOE_ACT_STATIC)
     return fail(MOE_EINVAL, "act_scheme = %d", d->act_scheme);
 
-  if (d->w_dtype == MOE_DT_FP8_E4M3) {
+  if (d->w_dtype == MOE_DT_FP4_E2M1) {
+    if (d->w_scale_fmt != MOE_SCALE_UE8M0) return fail(MOE_EINVAL, "fp4 experts need UE8M0 block scales");
+    if (d->w_layout != MOE_LAYOUT_PACKED)
+      return fail(MOE_EUNSUPPORTED, "fp4 experts run on packed weights only (moe_pack_weights)");
+  }
+  if (is_fp8(d)) {
     if (d->act_dtype != MOE_DT_BF16)
       return fail(MOE_EUNSUPPORTED, "fp8 experts need bf16 activations");
     if (d->w_scale_fmt == MOE_SCALE_NONE)
@@ -107,9 +121,13 @@ moe_status validate(const moe_desc* d) {
   }
   if (d->path == MOE_PATH_STREAM && (d->w_layout != MOE_LAYOUT_PACKED || d->T > kStreamMaxTokens))
     return fail(MOE_EUNSUPPORTED, "the weight-streaming path needs packed weights and T <= %d", kStreamMaxTokens);
-  if (d->path == MOE_PATH_STREAM && d->w_dtype == MOE_DT_FP8_E4M3 &&
+  if (d->path == MOE_PATH_STREAM && is_fp8(d) &&
       (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
     return fail(MOE_EUNSUPPORTED, "the fp8 weight-streaming path needs H, I <= %d", 128 * kStreamMaxScaleBlocks);
+  if (d->w_dtype == MOE_DT_FP4_E2M1 &&
+      (d->path == MOE_PATH_GROUPED || d->T > kStreamMaxTokens || d->H / 128 > kStreamMaxScaleBlocks ||
+       d->I / 128 > kStreamMaxScaleBlocks))
+    return fail(MOE_EUNSUPPORTED, "fp4 experts run on the weight-streaming path only (T <= %d)", kStreamMaxTokens);
   return MOE_OK;
 }
 
@@ -144,12 +162,12 @@ size_t packed_bytes(const moe_desc* d, int which) {
   const int64_t N = gate_up ? d->I : d->H;
   const int64_t K = gate_up ? d->H : d->I;
   const int64_t tiles = packed_tiles(gate_up, (int)N);
-  return (size_t)d->E * tiles * 256 * K * elt_bytes(d->w_dtype);
+  return (size_t)d->E * tiles * 256 * w_row_bytes(d->w_dtype, K);
 }
 
 // expert GEMMs stream the touched experts' weights (decode-sized batches)
 bool use_stream(const moe_desc* d) {
-  if (d->w_dtype == MOE_DT_FP8_E4M3 && (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
+  if (is_fp8(d) && (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
     return false;
   return packed(d) && d->T <= kStreamMaxTokens && (d->path == MOE_PATH_STREAM || d->path == MOE_PATH_AUTO);
 }
@@ -240,7 +258,7 @@ ForwardWs carve_forward(Carve& c, const moe_desc* d) {
     w.sched_gu = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
     w.sched_dn = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, down_ntiles(d))));
   }
-  w.h = c.take<uint8_t>((size_t)P * d->I * elt_bytes(d->w_dtype));
+  w.h = c.take<uint8_t>((size_t)P * d->I * (is_fp8(d) ? 1 : elt_bytes(d->w_dtype)));
   if (is_fp8(d)) w.hs = c.take<float>((size_t)P * (d->I / 128));
   w.y = c.take<uint8_t>((size_t)P * d->H * elt_bytes(d->y_dtype));
   if (use_stream(d)) w.partial = (float*)c.take<uint8_t>(stream_partial_bytes(d));
@@ -386,7 +404,7 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
   if (use_stream(d))
-    e = launch_gemm_stream(a, is_fp8(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
+    e = launch_gemm_stream(a, wfmt(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), st);
   else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
@@ -415,7 +433,7 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
   if (use_stream(d))
-    e = launch_gemm_stream(a, is_fp8(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
+    e = launch_gemm_stream(a, wfmt(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), st);
   else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
@@ -641,7 +659,7 @@ moe_status moe_pack_weights(const moe_desc* d, int which, const void* w0, const 
   if (!aligned16(w0) || (gate_up && !aligned16(w1)) || ((uintptr_t)dst & (kAlign - 1)))
     return fail(MOE_EINVAL, "weights must be 16-byte and dst 256-byte aligned");
   const int N = gate_up ? d->I : d->H;
-  const int64_t row_bytes = (int64_t)(gate_up ? d->H : d->I) * elt_bytes(d->w_dtype);
+  const int64_t row_bytes = w_row_bytes(d->w_dtype, gate_up ? d->H : d->I);
   MOE_TRY_HIP(launch_pack(w0, w1, gate_up, d->E, N, row_bytes, dst, (hipStream_t)stream), "pack launch");
   return MOE_OK;
 }

@@ -37,8 +37,12 @@ namespace {
 
 constexpr int kRowB = 64;       // packed bytes per row per K step
 constexpr int kChunk = 256 * kRowB;
-template <bool kFp8>
-constexpr int kRing = kFp8 ? 3 : 4;   // K steps in flight per wave
+template <int kW>
+constexpr int kRing = kW == 0 ? 4 : (kW == 1 ? 3 : 4);   // K steps in flight per wave (bf16, fp8, fp4)
+// waves per SIMD: fp4 steps carry twice the token bytes, so its deeper ring
+// takes the whole register file with one wave per SIMD
+template <int kW>
+constexpr int kWavesPerSimd = kW == 2 ? 1 : 2;
 
 __device__ __forceinline__ int pswz(int row, int chunk) {
   return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -48,10 +52,20 @@ __device__ __forceinline__ float wscale(const void* s, int ue8m0, int64_t idx) {
   return ue8m0 ? e8m0_to_f32(((const uint8_t*)s)[idx]) : ((const float*)s)[idx];
 }
 
-template <bool kFp8, int NT>
+// weight formats of the streaming GEMM
+constexpr int kWBf16 = 0, kWFp8 = 1, kWFp4 = 2;
+
+// K steps of 64 packed weight bytes: 32 bf16, 64 fp8 or 128 fp4 values
+template <int kW>
+__host__ __device__ inline int stream_steps(int K) {
+  return kW == kWBf16 ? K * 2 / kRowB : (kW == kWFp8 ? K / kRowB : K / (2 * kRowB));
+}
+
+template <int kW, int NT>
 struct Step {
-  i32x4 a[2][2];    // [weight tile][16-byte piece]
-  i32x4 b[NT][2];   // [token tile][16-byte piece]
+  i32x4 a[2][2];                       // [weight tile][16-byte piece]
+  i32x4 b[NT][kW == kWFp4 ? 4 : 2];    // [token tile][16-byte piece]
+  uint32_t s[kW == kWFp4 ? 2 : 1];     // fp4: the 4 UE8M0 block scales of each weight row's step
 };
 
 // Epilogue of one work item from its fp32 accumulators.  Lane holds token
@@ -137,15 +151,18 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
 // K steps [kt_begin, kt_end) of one work item.  With `part` the fp32
 // accumulators of the item's valid rows are stored there; otherwise the
 // epilogue runs.
-template <bool kFp8, int kMode, bool kOutF32, int NT>
+template <int kW, int kMode, bool kOutF32, int NT>
 __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& it, int kt_begin, int kt_end,
                                             float* part) {
+  constexpr bool kFp8 = kW != kWBf16;   // fp8 activations (fp8 and fp4 weights)
+  constexpr bool kFp4 = kW == kWFp4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
   const int e = it.expert;
   const int K = a.K, N = a.N;
-  const int elt = kFp8 ? 1 : 2;
-  const int KT = K * elt / kRowB;
+  const int elt = kFp8 ? 1 : 2;         // bytes per activation element
+  const int KT = stream_steps<kW>(K);
+  const int kstep_b = kFp4 ? 2 * kRowB : kRowB;   // activation bytes per K step
 
   // weight rows (packed tile rows) of this lane
   int arow[2];
@@ -158,12 +175,33 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   }
   const uint8_t* abase = (const uint8_t*)a.w0 + ((int64_t)e * a.wtiles + it.ntile) * KT * (int64_t)kChunk;
   // byte offsets of the two 16-byte pieces this lane needs per weight row:
-  // bf16: logical chunks 2*kk + hl (kk = 0, 1); fp8: 2*hl and 2*hl + 1
+  // bf16: logical chunks 2*kk + hl (kk = 0, 1); fp8: 2*hl and 2*hl + 1;
+  // fp4: 2*m + hl for the step's two 64-deep MFMAs m (the fp4 A operand of a
+  // lane half holds 32 consecutive K)
   int aoff[2][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) aoff[t][q] = pswz(arow[t], kFp8 ? hl * 2 + q : q * 2 + hl);
+    for (int q = 0; q < 2; ++q) aoff[t][q] = pswz(arow[t], (kFp8 && !kFp4) ? hl * 2 + q : q * 2 + hl);
+  // fp4: UE8M0 scales [rows, K/32] of this lane's two weight rows
+  const uint8_t* srow[2] = {nullptr, nullptr};
+  if constexpr (kFp4) {
+    const int KS = K / 32;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      int ch;
+      const uint8_t* sm;
+      if (kMode == 0) {
+        ch = it.ntile * 128 + (arow[t] & 127);
+        sm = (const uint8_t*)(arow[t] < 128 ? a.s0 : a.s1);
+      } else {
+        ch = it.ntile * 256 + arow[t];
+        sm = (const uint8_t*)a.s0;
+      }
+      ch = ch < N ? ch : N - 1;   // rows past N are zero in the packed tile
+      srow[t] = sm + ((int64_t)e * N + ch) * KS;
+    }
+  }
   // token rows of this lane
   int64_t src_row[NT];
   const uint8_t* brow[NT];
@@ -174,14 +212,18 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
     src_row[j] = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
     brow[j] = (const uint8_t*)a.act + src_row[j] * (int64_t)K * elt;
   }
-  // byte offsets (within a K step) of the token pieces, same K mapping as A
-  int boff[2];
+  // byte offsets (within a K step) of the token pieces, same K mapping as A;
+  // fp4 steps hold two 64-deep MFMAs, whose fp8 B operand of a lane half is
+  // K hb*16 .. +16 and 32 + hb*16 .. +16 of the MFMA's 64
+  constexpr int kBP = kFp4 ? 4 : 2;
+  int boff[kBP];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) boff[q] = (kFp8 ? hl * 2 + q : q * 2 + hl) * 16;
+  for (int q = 0; q < kBP; ++q)
+    boff[q] = kFp4 ? q * 32 + hl * 16 : ((kFp8 ? hl * 2 + q : q * 2 + hl) * 16);
 
   const int KB = K / 128;
 
-  typedef Step<kFp8, NT> S;
+  typedef Step<kW, NT> S;
   auto load = [&](S& st, int kt) {
     const uint8_t* ck = abase + (int64_t)kt * kChunk;
 #pragma unroll
@@ -191,7 +233,11 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) st.b[j][q] = *(const i32x4*)(brow[j] + (int64_t)kt * kRowB + boff[q]);
+      for (int q = 0; q < kBP; ++q) st.b[j][q] = *(const i32x4*)(brow[j] + (int64_t)kt * kstep_b + boff[q]);
+    if constexpr (kFp4) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) st.s[t] = *(const uint32_t*)(srow[t] + kt * 4);
+    }
   };
 
   f32x16 acc[2][NT];
@@ -215,7 +261,7 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
         const int64_t src = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
         s_sx[i] = a.act_scales[src * KB + kb];
       }
-      for (int i = tid; i < 2 * KB; i += 256) {
+      for (int i = tid; i < (kFp4 ? 0 : 2 * KB); i += 256) {
         const int h = i / KB, kb = i - h * KB;
         if (kMode == 0) {
           s_sw[h][kb] = wscale(h == 0 ? a.s0 : a.s1, a.scale_ue8m0, ((int64_t)e * NBr + it.ntile) * KB + kb);
@@ -230,7 +276,30 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   };
 
   auto consume = [&](const S& st, int kt) {
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+      // two 64-deep MFMAs per step, the weights' block scales applied by the
+      // MFMA (lane half hl: block 2*m + hl of the step), the activation scale
+      // of the step's 128-deep block by promotion
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const float sx = s_sx[(j * 32 + l32) * KB + kt];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x16 p = {};
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const i32x8 av = {st.a[t][m].x, st.a[t][m].y, st.a[t][m].z, st.a[t][m].w, 0, 0, 0, 0};
+            const i32x8 bv = {st.b[j][2 * m].x, st.b[j][2 * m].y, st.b[j][2 * m].z, st.b[j][2 * m].w,
+                              st.b[j][2 * m + 1].x, st.b[j][2 * m + 1].y, st.b[j][2 * m + 1].z,
+                              st.b[j][2 * m + 1].w};
+            const int sa = (int)((st.s[t] >> (8 * (2 * m + hl))) & 0xff);
+            p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, p, 4, 0, 0, sa, 0, 127);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][j][r] = __builtin_fmaf(p[r], sx, acc[t][j][r]);
+        }
+      }
+    } else if constexpr (kFp8) {
       // each step's partial sum is promoted on its own (both 64-deep halves
       // of a 128-deep scale block carry the same scales)
       const int kb = kt >> 1;
@@ -262,7 +331,7 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   };
 
   // register ring: K steps kt .. kt+kRing-1 in flight
-  constexpr int R = kRing<kFp8>;
+  constexpr int R = kRing<kW>;
   S ring[R];
   int kt0 = kt_begin;
   if (kt_end - kt_begin >= 2 * R) {
@@ -317,10 +386,10 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
 }
 
-template <bool kFp8, int kMode, bool kOutF32>
-__global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a) {
+template <int kW, int kMode, bool kOutF32>
+__global__ __launch_bounds__(256, kWavesPerSimd<kW>) void gemm_stream_kernel(GemmArgs a) {
   const int items = a.sched->total;
-  const int KT = a.K * (kFp8 ? 1 : 2) / kRowB;
+  const int KT = stream_steps<kW>(a.K);
   const int S = stream_splits(items, KT);
   const int u = xcd_work_index(items * S);
   if (u < 0) return;
@@ -329,9 +398,9 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a) {
   const int kt0 = (int)((int64_t)KT * sp / S), kt1 = (int)((int64_t)KT * (sp + 1) / S);
   float* part = S > 1 ? a.partial + (int64_t)u * kStreamPartFloats : nullptr;
   if (it.row_end - it.row_begin > 32)
-    stream_tile<kFp8, kMode, kOutF32, 2>(a, it, kt0, kt1, part);
+    stream_tile<kW, kMode, kOutF32, 2>(a, it, kt0, kt1, part);
   else
-    stream_tile<kFp8, kMode, kOutF32, 1>(a, it, kt0, kt1, part);
+    stream_tile<kW, kMode, kOutF32, 1>(a, it, kt0, kt1, part);
 }
 
 // Split-K reduction: one workgroup per work item sums its S partial tiles in
@@ -339,10 +408,11 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a) {
 // Nothing to do when S == 1.  Partial tile layout: part[row * 256 + c] with,
 // for gate/up, the gate value of channel ntile*128 + w*32 + x at c = w*64 + x
 // and its up value at c = w*64 + 32 + x; for down, channel ntile*256 + c.
-template <bool kFp8, int kMode, bool kOutF32>
+template <int kW, int kMode, bool kOutF32>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
+  constexpr bool kFp8 = kW != kWBf16;   // fp8 activations and h (fp8 and fp4 weights)
   const int items = a.sched->total;
-  const int KT = a.K * (kFp8 ? 1 : 2) / kRowB;
+  const int KT = stream_steps<kW>(a.K);
   const int S = stream_splits(items, KT);
   const int w = blockIdx.x;
   if (S == 1 || w >= items) return;
@@ -424,32 +494,28 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, int reduce_grid, hipStream_t stream) {
+hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   dim3 g(grid), rg(reduce_grid), b(256);
-  if (fp8) {
-    if (mode == 0) {
-      hipLaunchKernelGGL((gemm_stream_kernel<true, 0, false>), g, b, 0, stream, a);
-      hipLaunchKernelGGL((stream_reduce_kernel<true, 0, false>), rg, b, 0, stream, a);
-    } else if (a.out_f32) {
-      hipLaunchKernelGGL((gemm_stream_kernel<true, 1, true>), g, b, 0, stream, a);
-      hipLaunchKernelGGL((stream_reduce_kernel<true, 1, true>), rg, b, 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((gemm_stream_kernel<true, 1, false>), g, b, 0, stream, a);
-      hipLaunchKernelGGL((stream_reduce_kernel<true, 1, false>), rg, b, 0, stream, a);
-    }
+#define MOE_STREAM_LAUNCH(W, M, F32)                                                   \
+  do {                                                                                 \
+    hipLaunchKernelGGL((gemm_stream_kernel<W, M, F32>), g, b, 0, stream, a);           \
+    hipLaunchKernelGGL((stream_reduce_kernel<W, M, F32>), rg, b, 0, stream, a);        \
+  } while (0)
+  if (wfmt == kWFp4) {
+    if (mode == 0) MOE_STREAM_LAUNCH(kWFp4, 0, false);
+    else if (a.out_f32) MOE_STREAM_LAUNCH(kWFp4, 1, true);
+    else MOE_STREAM_LAUNCH(kWFp4, 1, false);
+  } else if (wfmt == kWFp8) {
+    if (mode == 0) MOE_STREAM_LAUNCH(kWFp8, 0, false);
+    else if (a.out_f32) MOE_STREAM_LAUNCH(kWFp8, 1, true);
+    else MOE_STREAM_LAUNCH(kWFp8, 1, false);
   } else {
-    if (mode == 0) {
-      hipLaunchKernelGGL((gemm_stream_kernel<false, 0, false>), g, b, 0, stream, a);
-      hipLaunchKernelGGL((stream_reduce_kernel<false, 0, false>), rg, b, 0, stream, a);
-    } else if (a.out_f32) {
-      hipLaunchKernelGGL((gemm_stream_kernel<false, 1, true>), g, b, 0, stream, a);
-      hipLaunchKernelGGL((stream_reduce_kernel<false, 1, true>), rg, b, 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((gemm_stream_kernel<false, 1, false>), g, b, 0, stream, a);
-      hipLaunchKernelGGL((stream_reduce_kernel<false, 1, false>), rg, b, 0, stream, a);
-    }
+    if (mode == 0) MOE_STREAM_LAUNCH(kWBf16, 0, false);
+    else if (a.out_f32) MOE_STREAM_LAUNCH(kWBf16, 1, true);
+    else MOE_STREAM_LAUNCH(kWBf16, 1, false);
   }
+#undef MOE_STREAM_LAUNCH
   return hipGetLastError();
 }
 

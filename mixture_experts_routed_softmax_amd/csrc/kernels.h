@@ -100,7 +100,8 @@ constexpr int kPackedDownChannels = 256;     // output channels per packed down 
 // touched expert), split over K when there are few items, plus its split-K
 // reduction launch (reduce_grid >= min(item capacity, kStreamTarget): only
 // fewer than kStreamTarget items are ever split)
-hipError_t launch_gemm_stream(const GemmArgs& a, int fp8, int mode, int grid, int reduce_grid, hipStream_t stream);
+// wfmt: weight format, 0 bf16, 1 fp8, 2 fp4 (fp8 activations for 1 and 2)
+hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, hipStream_t stream);
 constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamMaxScaleBlocks = 64;   // fp8 streaming: K / 128 at most (K <= 8192)
 constexpr int kStreamTarget = 1024;      // work units the split aims for (two rounds of 2 per CU)

@@ -13,7 +13,9 @@ import mixture_experts_routed_softmax_amd as moe
 import oracle
 import synthetic
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+# fp4 experts quantize activations and h exactly as fp8 experts do (their
+# weights are exact on both sides), so they share the fp8 tolerance
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "fp4": 6e-2}
 
 
 def tol_of(s: synthetic.LayerSpec) -> float:
@@ -25,7 +27,7 @@ def desc_for(s: synthetic.LayerSpec, T: int | None = None, path: str = "auto", y
     return moe.make_desc(s.T if T is None else T, s.H, s.I, s.E, s.k, score=s.score,
                          renormalize=s.renormalize, routed_scale=s.routed_scale,
                          act_dtype=s.act, w_dtype=s.experts,
-                         w_scale_fmt=s.scale_fmt if s.experts == "fp8" else "none",
+                         w_scale_fmt=s.scale_fmt if s.experts in ("fp8", "fp4") else "none",
                          y_dtype=y_dtype, path=path, layout=layout, gate=s.gate)
 
 
@@ -47,10 +49,10 @@ def host(layer: dict) -> dict:
 
 def oracle_experts(s, hl: dict) -> oracle.Experts:
     gate = {"silu": oracle.GATE_SILU, "gelu": oracle.GATE_GELU, "relu": oracle.GATE_RELU}[s.gate]
-    if s.experts == "fp8":
+    if s.experts in ("fp8", "fp4"):
         fmt = oracle.SCALE_UE8M0 if s.scale_fmt == "ue8m0" else oracle.SCALE_F32
         return oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], hl["s_gate"], hl["s_up"],
-                              hl["s_down"], fmt, s.block, act_fp8=True, gate=gate)
+                              hl["s_down"], fmt, s.block, act_fp8=True, gate=gate, fp4=s.experts == "fp4")
     return oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], gate=gate)
 
 
@@ -136,7 +138,7 @@ def run_staged(s, L: dict, ids_in: torch.Tensor, w_in: torch.Tensor, y_dtype=Non
     wg, wu, wd = expert_weights(d, L)
     dev = L["x"].device
     P = T * s.k
-    fp8 = s.experts == "fp8"
+    fp8 = s.experts in ("fp8", "fp4")
     r = {}
     r["counts"] = torch.empty(s.E, dtype=torch.int32, device=dev)
     r["offsets"] = torch.empty(s.E + 1, dtype=torch.int32, device=dev)

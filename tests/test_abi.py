@@ -96,6 +96,28 @@ def test_validation_rejects(bad, status):
     assert moe.moe_last_error() != ""
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(layout="rowmajor"), moe.MOE_EUNSUPPORTED),     # fp4 runs on packed weights only
+    (dict(w_scale_fmt="f32"), moe.MOE_EINVAL),          # fp4 scales are UE8M0
+    (dict(T=4096), moe.MOE_EUNSUPPORTED),               # weight-streaming path only (T <= 64)
+    (dict(path="grouped"), moe.MOE_EUNSUPPORTED),
+])
+def test_fp4_validation(over, status):
+    base = dict(score="sigmoid", renormalize=True, routed_scale=2.5, act_dtype="bf16", w_dtype="fp4",
+                w_scale_fmt="ue8m0", layout="packed")
+    T = over.pop("T", 64)
+    base.update(over)
+    d = moe.make_desc(T, 7168, 2048, 256, 8, **base)
+    assert _status_of(_forward_nulls, d) == status
+
+
+def test_fp4_packed_bytes():
+    d = moe.make_desc(64, 7168, 2048, 256, 8, w_dtype="fp4", w_scale_fmt="ue8m0", layout="packed")
+    # half the bytes of the fp8 packing: E * ceil(I/128) tiles * 256 rows * H/2
+    assert moe.moe_packed_weight_bytes(d, moe.MOE_PACK_GATE_UP) == 256 * 16 * 256 * 3584
+    assert moe.moe_packed_weight_bytes(d, moe.MOE_PACK_DOWN) == 256 * 28 * 256 * 1024
+
+
 def test_fp8_static_activation_rejected():
     d = _ds_fp8(act_scheme="static")
     assert _status_of(_forward_nulls, d) == moe.MOE_EUNSUPPORTED

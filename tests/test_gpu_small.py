@@ -81,7 +81,7 @@ def test_staged_small(name, layout):
     assert np.array_equal(r["perm"].cpu().numpy(), perm_o)
     assert np.array_equal(r["inv"].cpu().numpy(), inv_o)
     tok = perm_o // s.k
-    if s.experts == "fp8":
+    if s.experts in ("fp8", "fp4"):
         codes_o, scales_o = oracle.quant_rows(hl["x"], 128)
         # compare code values (the GPU encodes -0 as 0x80, the oracle as 0x00)
         xs = r["x_sorted"].cpu().view(torch.float8_e4m3fn).float().numpy()
@@ -95,7 +95,7 @@ def test_staged_small(name, layout):
     ex = oracle_experts(s, hl)
     rows = coverage_rows(offsets_o, 64)
     h_o, y_o = ex.pairs(hl["x"], tok[rows], ids_o.reshape(-1)[perm_o[rows]])
-    if s.experts == "fp8":
+    if s.experts in ("fp8", "fp4"):
         h = dequant_rows(r["h"][torch.from_numpy(rows).cuda()], r["h_scales"][torch.from_numpy(rows).cuda()])
     else:
         h = r["h"].cpu().float().numpy()[rows]
@@ -232,6 +232,11 @@ STREAM = {
     "bf16_decode_split_hot": synthetic.spec("qwen_decode", T=64, H=512, I=256, E=4, k=2),
     "fp8_decode_split": synthetic.spec("dsv3_fp8", T=8, H=1024, I=512, E=16, k=4),
     "fp8_decode_split_hot_ue8m0": synthetic.spec("dsv3_fp8", T=64, H=1024, I=512, E=4, k=2, scale_fmt="ue8m0"),
+    # int8-packed FP4 experts (UE8M0 per row per 32 K): one tile per item,
+    # split K, and experts with more than 32 rows
+    "fp4_decode": synthetic.spec("dsv3_fp4", T=24, H=256, I=384, E=16, k=4),
+    "fp4_decode_split": synthetic.spec("dsv3_fp4", T=8, H=1024, I=512, E=16, k=4),
+    "fp4_decode_split_hot": synthetic.spec("dsv3_fp4", T=64, H=1024, I=512, E=4, k=2),
 }
 
 
@@ -311,7 +316,7 @@ GATE_CASES = [(g, name, layout, path) for g in ("gelu", "relu") for name, layout
     ("tiny", "rowmajor", "grouped"), ("bf16_softmax", "rowmajor", "grouped"),
     ("bf16_softmax", "packed", "grouped"), ("fp8_f32", "rowmajor", "grouped"),
     ("fp8_ue8m0", "packed", "grouped"), ("bf16_decode_split_hot", "packed", "stream"),
-    ("fp8_decode_split", "packed", "stream")]]
+    ("fp8_decode_split", "packed", "stream"), ("fp4_decode_split", "packed", "stream")]]
 
 
 @pytest.mark.parametrize("gate,name,layout,path", GATE_CASES)
