@@ -124,10 +124,6 @@ moe_status validate(const moe_desc* d) {
   if (d->path == MOE_PATH_STREAM && is_fp8(d) &&
       (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
     return fail(MOE_EUNSUPPORTED, "the fp8 weight-streaming path needs H, I <= %d", 128 * kStreamMaxScaleBlocks);
-  if (d->w_dtype == MOE_DT_FP4_E2M1 &&
-      (d->path == MOE_PATH_GROUPED || d->T > kStreamMaxTokens || d->H / 128 > kStreamMaxScaleBlocks ||
-       d->I / 128 > kStreamMaxScaleBlocks))
-    return fail(MOE_EUNSUPPORTED, "fp4 experts run on the weight-streaming path only (T <= %d)", kStreamMaxTokens);
   return MOE_OK;
 }
 
@@ -406,7 +402,7 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), st);
-  else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 0, grid, st);
+  else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
   else e = launch_gate_up_fp8(a, grid, st);
@@ -435,7 +431,7 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), st);
-  else if (packed(d)) e = launch_gemm_packed(a, is_fp8(d), 1, grid, st);
+  else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);
   else e = launch_down_fp8(a, grid, st);

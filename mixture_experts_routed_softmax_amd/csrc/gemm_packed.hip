@@ -48,19 +48,30 @@ constexpr int kRowB = 64;                // bytes per LDS row per K step
 constexpr int kA = kRows * kRowB;        // 16 KB of weights per stage
 constexpr int kLdsBudget = 160 * 1024;
 
+// weight formats: bf16, fp8 (e4m3) and fp4 (e2m1, two per byte); fp8 and
+// fp4 experts take e4m3 activations
+constexpr int kWBf16 = 0, kWFp8 = 1, kWFp4 = 2;
+
 // token rows per tile: 256 for bf16 (each wave 64 weight rows x 128 tokens),
-// 128 for fp8 (each wave 64 x 64; the per-block promotion needs a second set
-// of accumulators)
-template <bool kFp8>
+// 128 for fp8 / fp4 (each wave 64 x 64; the per-block promotion needs a
+// second set of accumulators).  A K step is 64 weight bytes per row: 32 bf16,
+// 64 fp8 or 128 fp4 values, so an fp4 step carries 128 activation bytes per
+// token row and the weight rows' 4 UE8M0 block scales (one dword per row).
+template <int kW>
 struct Geo {
-  static constexpr int kTok = kFp8 ? 128 : 256;
+  static constexpr int kTok = kW != kWBf16 ? 128 : 256;
   static constexpr int kNTW = kTok / 64;            // token tiles per wave
-  static constexpr int kB = kTok * kRowB;           // token bytes per stage
-  static constexpr int kStage = kA + kB;
-  static constexpr int kAmax = kFp8 ? 4 * kTok * 4 : 0;     // fp8 epilogue scratch
-  static constexpr int kStages = (kLdsBudget - kAmax) / kStage;   // 6 (fp8) or 5 (bf16)
-  static constexpr int kLoads = 2 + kTok / 128;     // DMA instructions per thread per stage
+  static constexpr int kTokRowB = kW == kWFp4 ? 128 : kRowB;   // activation bytes per token row and step
+  static constexpr int kB = kTok * kTokRowB;        // token bytes per stage
+  static constexpr int kSc = kW == kWFp4 ? kRows * 4 : 0;      // fp4 weight scales per stage
+  static constexpr int kStage = kA + kB + kSc;
+  static constexpr int kAmax = kW != kWBf16 ? 4 * kTok * 4 : 0;     // fp8 epilogue scratch
+  static constexpr int kStages = (kLdsBudget - kAmax) / kStage;   // 6 (fp8), 5 (bf16) or 4 (fp4)
+  static constexpr int kLoads = 2 + kB / 8192 + (kW == kWFp4 ? 1 : 0);   // DMA instructions per thread per stage
 };
+
+// fp4 token rows: 128 bytes, 16-byte chunk c of row r at chunk c ^ (r & 7)
+__device__ __forceinline__ int swz128(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -92,7 +103,8 @@ __device__ __forceinline__ void wait_steps(int ahead) {
     case 1: wait_vmcnt<kLoads>(); break;
     case 2: wait_vmcnt<2 * kLoads>(); break;
     case 3: wait_vmcnt<3 * kLoads>(); break;
-    default: wait_vmcnt<4 * kLoads>(); break;
+    case 4: wait_vmcnt<4 * kLoads>(); break;
+    default: wait_vmcnt<5 * kLoads>(); break;
   }
 }
 
@@ -101,19 +113,24 @@ __device__ __forceinline__ float wscale(const void* s, int ue8m0, int64_t idx) {
 }
 
 // fragments of one K step: two weight tiles and the wave's token tiles
-template <bool kFp8>
+// (fp4: 16-byte e2m1 weight fragments and the rows' scale dwords)
+template <int kW>
 struct Frag {
-  typedef typename std::conditional<kFp8, i32x8, bf16x8>::type T;
-  static constexpr int kK = kFp8 ? 1 : 2;   // MFMAs along K per step
-  T a[kK][2];
-  T b[kK][Geo<kFp8>::kNTW];
+  typedef typename std::conditional<kW != kWBf16, i32x8, bf16x8>::type T;
+  typedef typename std::conditional<kW == kWFp4, i32x4, T>::type TA;
+  static constexpr int kK = kW == kWFp8 ? 1 : 2;   // MFMAs along K per step
+  TA a[kK][2];
+  T b[kK][Geo<kW>::kNTW];
+  uint32_t s[kW == kWFp4 ? 2 : 1];
 };
 
-template <bool kFp8, int kMode, bool kOutF32>
+template <int kW, int kMode, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
-  typedef Geo<kFp8> G;
+  constexpr bool kFp8 = kW != kWBf16;   // e4m3 activations (fp8 and fp4 weights)
+  constexpr bool kFp4 = kW == kWFp4;
+  typedef Geo<kW> G;
   constexpr int kTok = G::kTok, kNTW = G::kNTW, kB = G::kB, kStage = G::kStage, kStages = G::kStages;
-  constexpr int kLoads = G::kLoads;
+  constexpr int kLoads = G::kLoads, kTokRowB = G::kTokRowB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
   const int w = xcd_work_index(a.sched->total);
   if (w < 0) return;
@@ -123,8 +140,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
   const int rg = wave & 3, tg = wave >> 2;
   const int e = it.expert;
   const int K = a.K, N = a.N;
-  const int elt = kFp8 ? 1 : 2;
-  const int KT = K * elt / kRowB;          // K steps
+  const int elt = kFp8 ? 1 : 2;            // bytes per activation element
+  const int KT = kFp4 ? K / 128 : K * elt / kRowB;   // K steps
   const int valid = it.row_end - it.row_begin;
   const int ntok = (valid + 31) >> 5;
   int my_nt = ntok - kNTW * tg;            // live token tiles of this wave (0..kNTW)
@@ -133,16 +150,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
   // ---- loaders
   const uint8_t* abase = (const uint8_t*)a.w0 + ((int64_t)e * a.wtiles + it.ntile) * KT * (int64_t)kA;
   // token rows: DMA instruction i of wave w fills LDS rows (i*8 + w)*16 .. +16
-  constexpr int kBI = kTok / 128;
+  // (fp4: 128-byte rows, (i*8 + w)*8 .. +8)
+  constexpr int kBI = kB / 8192;
   const uint8_t* bsrc[kBI];
 #pragma unroll
   for (int i = 0; i < kBI; ++i) {
-    const int row = (i * 8 + wave) * 16 + (lane >> 2);
+    const int row = kFp4 ? (i * 8 + wave) * 8 + (lane >> 3) : (i * 8 + wave) * 16 + (lane >> 2);
     int r = it.row_begin + row;
     r = r < it.row_end ? r : it.row_end - 1;
     const int64_t src_row = a.gather ? (int64_t)(a.gather[r] / a.gather_div) : (int64_t)r;
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int c = kFp4 ? ((lane & 7) ^ (row & 7)) : ((lane & 3) ^ ((row >> 2) & 3));
     bsrc[i] = (const uint8_t*)a.act + src_row * (int64_t)K * elt + c * 16;
+  }
+  // fp4: UE8M0 scale dword (the step's 4 blocks) of tile row (wave & 3)*64 + lane;
+  // waves 4-7 repeat waves 0-3 so that every wave issues the same loads
+  const uint8_t* ssrc = nullptr;
+  if constexpr (kFp4) {
+    const int row = (wave & 3) * 64 + lane;
+    int ch;
+    const uint8_t* sm;
+    if (kMode == 0) {
+      ch = it.ntile * 128 + (row & 127);
+      sm = (const uint8_t*)(row < 128 ? a.s0 : a.s1);
+    } else {
+      ch = it.ntile * 256 + row;
+      sm = (const uint8_t*)a.s0;
+    }
+    ch = ch < N ? ch : N - 1;   // rows past N are zero in the packed tile
+    ssrc = sm + ((int64_t)e * N + ch) * (K / 32);
   }
   // wave-uniform parts of the DMA addresses (M0 takes the LDS address)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -153,7 +188,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     lds_load16(src, sb);
     lds_load16(src + 8192, sb + 8192);
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) lds_load16(bsrc[i] + (int64_t)kt * kRowB, sb + kA + i * 8192);
+    for (int i = 0; i < kBI; ++i) lds_load16(bsrc[i] + (int64_t)kt * kTokRowB, sb + kA + i * 8192);
+    if constexpr (kFp4)
+      __builtin_amdgcn_global_load_lds(ssrc + kt * 4, (lds_ptr)(smem + stage * kStage + kA + kB + (wv & 3) * 256), 4,
+                                       0, 0);
   };
 
   // LDS rows of this wave's tiles
@@ -167,17 +205,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
   }
   const int brow = tg * kNTW * 32;
 
-  typedef Frag<kFp8> F;
+  typedef Frag<kW> F;
   // The fragments of a K step are consumed in two halves (bf16: the two
-  // 16-deep MFMA K slices; fp8: token tile 0, then the weight tiles with the
-  // other token tiles).  A half is refilled from the next step's stage as
+  // 16-deep MFMA K slices; fp4: the two 64-deep MFMA K slices; fp8: token
+  // tile 0, then the weight tiles with the other token tiles).  A half is refilled from the next step's stage as
   // soon as its MFMAs are issued, so the LDS reads of step s+1 overlap the
   // MFMAs of step s without a second register set.
   auto read_half = [&](int stage, F& f, auto h_const, auto nt_const) {
     constexpr int NT = decltype(nt_const)::value, h = decltype(h_const)::value;
     const uint8_t* sa = smem + stage * kStage;
     const uint8_t* sb = sa + kA;
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+      // K slice h (64 deep): the e2m1 A operand of a lane half holds 32
+      // consecutive K (weight chunk 2h + hl); the e4m3 B operand holds K
+      // hl*16 .. +16 and 32 + hl*16 .. +16 of the slice (token chunks
+      // 4h + hl and 4h + 2 + hl).  The scale dwords of the weight rows are
+      // read first in the second slice's refill: the current step's second
+      // slice has used them by then, and the next step's first slice waits
+      // for them together with its own fragments
+      if constexpr (h == 1) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) f.s[t] = *(const uint32_t*)(sb + kB + (arow[t] + l32) * 4);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) f.a[h][t] = *(const i32x4*)(sa + swz(arow[t] + l32, h * 2 + hl));
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int row = brow + j * 32 + l32;
+        const i32x4 lo = *(const i32x4*)(sb + swz128(row, 4 * h + hl));
+        const i32x4 hi = *(const i32x4*)(sb + swz128(row, 4 * h + 2 + hl));
+        f.b[h][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+    } else if constexpr (kFp8) {
       auto ld8 = [&](const uint8_t* base, int row) {
         i32x4 lo = *(const i32x4*)(base + swz(row, hl * 2));
         i32x4 hi = *(const i32x4*)(base + swz(row, hl * 2 + 1));
@@ -235,7 +294,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
 
   auto mfma_half = [&](const F& f, auto h_const, auto nt_const) {
     constexpr int NT = decltype(nt_const)::value, h = decltype(h_const)::value;
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+      // e2m1 x e4m3, the weight row's block scale (block 2h + hl of the step)
+      // applied by the MFMA; the activation scale by the promotion
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int sc = (int)((f.s[t] >> (8 * (2 * h + hl))) & 0xff);
+        const i32x8 av = {f.a[h][t].x, f.a[h][t].y, f.a[h][t].z, f.a[h][t].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          part[t][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, f.b[h][j], part[t][j], 4, 0, 0, sc, 0, 127);
+      }
+    } else if constexpr (kFp8) {
       constexpr int j0 = h == 0 ? 0 : 1, j1 = h == 0 ? (NT < 1 ? NT : 1) : NT;
 #pragma unroll
       for (int j = j0; j < j1; ++j)
@@ -252,10 +322,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     }
   };
   // fp8: at the end of a 128-deep scale block (every second step) fold the
-  // block's partial sums into the accumulators with s_w(block) * s_x(row, block)
+  // block's partial sums into the accumulators with s_w(block) * s_x(row, block);
+  // fp4: every step is one 128-deep activation block, weights already scaled
   auto promote = [&](int kt, auto nt_const) {
     constexpr int NT = decltype(nt_const)::value;
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const float sx = sa_row[j][kt];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][j][r] = __builtin_fmaf(part[t][j][r], sx, acc[t][j][r]);
+          part[t][j] = f32x16{};
+        }
+      }
+    } else if constexpr (kFp8) {
       if (kt & 1) {
         const int kb = kt >> 1;
         const float s0 = wscale(a.s0, a.scale_ue8m0, sw_idx0 + kb);
@@ -293,12 +375,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     // from LDS stage `next` half by half as the MFMAs free their registers.
     auto body = [&](int s, int next) {
       __builtin_amdgcn_sched_barrier(0);
-      wait_lgkm<kFp8 ? 0 : 2 + NT>();   // this step's first half landed
+      // this step's first half landed (fp4: and the scales, read before the
+      // second half's fragments, which may still be in flight)
+      wait_lgkm<kFp4 ? 2 + 2 * NT : (kFp8 ? 0 : 2 + NT)>();
       mfma_half(f, h0, nt_const);
       __builtin_amdgcn_sched_barrier(0);
       read_half(next, f, h0, nt_const);
       __builtin_amdgcn_sched_barrier(0);
-      wait_lgkm<kFp8 ? (NT >= 1 ? 2 : 0) : 2 + NT>();   // ... and its second half
+      wait_lgkm<kFp4 ? 2 + 2 * NT : (kFp8 ? (NT >= 1 ? 2 : 0) : 2 + NT)>();   // ... and its second half
       mfma_half(f, h1, nt_const);
       __builtin_amdgcn_sched_barrier(0);
       read_half(next, f, h1, nt_const);
@@ -418,18 +502,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm_packed(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream) {
+hipError_t launch_gemm_packed(const GemmArgs& a, int wfmt, int mode, int grid, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   dim3 g(grid), b(kThreads);
-  if (fp8) {
-    if (mode == 0) hipLaunchKernelGGL((gemm_packed_kernel<true, 0, false>), g, b, 0, stream, a);
-    else if (a.out_f32) hipLaunchKernelGGL((gemm_packed_kernel<true, 1, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_packed_kernel<true, 1, false>), g, b, 0, stream, a);
-  } else {
-    if (mode == 0) hipLaunchKernelGGL((gemm_packed_kernel<false, 0, false>), g, b, 0, stream, a);
-    else if (a.out_f32) hipLaunchKernelGGL((gemm_packed_kernel<false, 1, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_packed_kernel<false, 1, false>), g, b, 0, stream, a);
-  }
+#define MOE_PACKED_LAUNCH(W)                                                                   \
+  do {                                                                                         \
+    if (mode == 0) hipLaunchKernelGGL((gemm_packed_kernel<W, 0, false>), g, b, 0, stream, a);  \
+    else if (a.out_f32) hipLaunchKernelGGL((gemm_packed_kernel<W, 1, true>), g, b, 0, stream, a); \
+    else hipLaunchKernelGGL((gemm_packed_kernel<W, 1, false>), g, b, 0, stream, a);            \
+  } while (0)
+  if (wfmt == kWFp4) MOE_PACKED_LAUNCH(kWFp4);
+  else if (wfmt == kWFp8) MOE_PACKED_LAUNCH(kWFp8);
+  else MOE_PACKED_LAUNCH(kWBf16);
+#undef MOE_PACKED_LAUNCH
   return hipGetLastError();
 }
 

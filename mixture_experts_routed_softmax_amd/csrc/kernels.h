@@ -93,7 +93,8 @@ hipError_t launch_gate_up_fp8(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_down_fp8(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t stream);
 // grouped GEMM on tile-packed weights (bf16 or fp8), mode 0 gate/up, 1 down
-hipError_t launch_gemm_packed(const GemmArgs& a, int fp8, int mode, int grid, hipStream_t stream);
+// wfmt: weight format, 0 bf16, 1 fp8, 2 fp4 (e4m3 activations for 1 and 2)
+hipError_t launch_gemm_packed(const GemmArgs& a, int wfmt, int mode, int grid, hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
 constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
 // weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per

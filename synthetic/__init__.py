@@ -95,6 +95,7 @@ TOKEN_COUNTS = {
     "qwen_decode": (1, 8, 32, 64),
     "dsv3_bf16": (8192,),
     "dsv3_fp8": (64, 8192),
+    "dsv3_fp4": (64, 8192),
 }
 
 

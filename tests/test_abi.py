@@ -99,8 +99,7 @@ def test_validation_rejects(bad, status):
 @pytest.mark.parametrize("over,status", [
     (dict(layout="rowmajor"), moe.MOE_EUNSUPPORTED),     # fp4 runs on packed weights only
     (dict(w_scale_fmt="f32"), moe.MOE_EINVAL),          # fp4 scales are UE8M0
-    (dict(T=4096), moe.MOE_EUNSUPPORTED),               # weight-streaming path only (T <= 64)
-    (dict(path="grouped"), moe.MOE_EUNSUPPORTED),
+    (dict(w_scale_fmt="none"), moe.MOE_EINVAL),
 ])
 def test_fp4_validation(over, status):
     base = dict(score="sigmoid", renormalize=True, routed_scale=2.5, act_dtype="bf16", w_dtype="fp4",

@@ -62,3 +62,10 @@ def test_dsv3_bf16_full():
 def test_dsv3_fp8_full(T, fmt):
     _full_case(synthetic.spec("dsv3_fp8", T=T, scale_fmt=fmt), seed=1, n_random=32,
                limit=160 if T > 64 else 64)
+
+
+@pytest.mark.parametrize("T", [64, 8192])
+def test_dsv3_fp4_full(T):
+    # int8-packed FP4 experts: the weight-streaming path at T = 64, the grouped
+    # GEMM at T = 8192
+    _full_case(synthetic.spec("dsv3_fp4", T=T), seed=2, n_random=32, limit=160 if T > 64 else 64)

@@ -23,6 +23,7 @@ SMALL = {
     "bf16_sigmoid": synthetic.spec("dsv3_bf16", T=130, H=256, I=256, E=16),
     "fp8_f32": synthetic.spec("dsv3_fp8", T=100, H=256, I=384, E=16, k=4),
     "fp8_ue8m0": synthetic.spec("dsv3_fp8", T=100, H=256, I=384, E=16, k=4, scale_fmt="ue8m0"),
+    "fp4": synthetic.spec("dsv3_fp4", T=100, H=256, I=384, E=16, k=4),
 }
 
 
@@ -31,7 +32,7 @@ def _layer(s, seed=0):
     return L, host(L)
 
 
-LAYOUTS = {name: (["rowmajor"] if s.experts == "f32" else ["rowmajor", "packed"])
+LAYOUTS = {name: (["rowmajor"] if s.experts == "f32" else (["packed"] if s.experts == "fp4" else ["rowmajor", "packed"]))
            for name, s in SMALL.items()}
 CASES = [(n, lay) for n in SMALL for lay in LAYOUTS[n]]
 
@@ -66,7 +67,7 @@ def test_staged_small(name, layout):
     # the router entry point alone
     ids = torch.empty(s.T, s.k, dtype=torch.int32, device="cuda")
     w = torch.empty(s.T, s.k, dtype=torch.float32, device="cuda")
-    d = desc_for(s)
+    d = desc_for(s, layout=layout)
     moe.moe_route_topk(d, L["x"], L["w_router"], L["router_bias"], ids, w, moe.workspace(d, moe.MOE_OP_ROUTE))
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ids_o)
@@ -316,7 +317,8 @@ GATE_CASES = [(g, name, layout, path) for g in ("gelu", "relu") for name, layout
     ("tiny", "rowmajor", "grouped"), ("bf16_softmax", "rowmajor", "grouped"),
     ("bf16_softmax", "packed", "grouped"), ("fp8_f32", "rowmajor", "grouped"),
     ("fp8_ue8m0", "packed", "grouped"), ("bf16_decode_split_hot", "packed", "stream"),
-    ("fp8_decode_split", "packed", "stream"), ("fp4_decode_split", "packed", "stream")]]
+    ("fp8_decode_split", "packed", "stream"), ("fp4_decode_split", "packed", "stream"),
+    ("fp4", "packed", "grouped")]]
 
 
 @pytest.mark.parametrize("gate,name,layout,path", GATE_CASES)
