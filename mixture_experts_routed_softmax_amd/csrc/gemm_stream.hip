@@ -38,7 +38,7 @@ namespace {
 constexpr int kRowB = 64;       // packed bytes per row per K step
 constexpr int kChunk = 256 * kRowB;
 template <int kW>
-constexpr int kRing = kW == 0 ? 4 : (kW == 1 ? 3 : 4);   // K steps in flight per wave (bf16, fp8, fp4)
+constexpr int kRing = kW == 0 ? 4 : (kW == 1 ? 3 : 5);   // K steps in flight per wave (bf16, fp8, fp4)
 // waves per SIMD: fp4 steps carry twice the token bytes, so its deeper ring
 // takes the whole register file with one wave per SIMD
 template <int kW>
