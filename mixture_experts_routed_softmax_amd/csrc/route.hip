@@ -184,6 +184,116 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
   }
 }
 
+// ------------------------------------------------- LDS-staged router (large T)
+// For large batches: a workgroup owns 64 tokens and all experts (padded to
+// kEP = 64, 128 or 256 rows) over a K slice.  The token and router rows of a
+// 64-deep K chunk are brought into LDS by global_load_lds (one 1 KB
+// instruction = 8 rows x 128 B, rows swizzled chunk ^ (row & 7)), 3 chunks in
+// flight, so each row is read once per workgroup in whole cache lines.
+// 8 waves; kWT = 8 / (kEP / 32) waves share a 32-expert tile: one wave takes
+// both token tiles, two waves one token tile each, four waves one token tile
+// and every other 16-deep slice (their partial tiles are added in a fixed
+// order).  The slice's logits go to part[slice][t][e] as in logits_kernel.
+constexpr int kBigTok = 64;
+constexpr int kRouteStages = 3;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from global memory straight into LDS (wave base + lane * 16)
+__device__ __forceinline__ void route_lds_load16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+template <int kEP>
+__global__ __launch_bounds__(512) void logits_lds_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wr, int64_t T, int H,
+                                                         int E, int chunks_per_slice, float* __restrict__ part) {
+  constexpr int kXB = kBigTok * 128;                  // token bytes per stage
+  constexpr int kStage = kXB + kEP * 128;
+  constexpr int kWI = kEP / 64;                       // router DMA instructions per wave per chunk
+  constexpr int kLoads = 1 + kWI;
+  constexpr int kET = kEP / 32, kWT = 8 / kET;       // expert tiles, waves per expert tile
+  constexpr int kNJ = kWT == 1 ? 2 : 1;               // token tiles per wave
+  constexpr int kUStep = kWT == 4 ? 2 : 1;            // 16-deep slices: every kUStep-th
+  static_assert((kEP + 1) * kBigTok * 4 <= kRouteStages * kStage, "logit tile fits the ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRouteStages * kStage];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * kBigTok;
+  const int nchunks = H / 64;
+  const int c0 = blockIdx.y * chunks_per_slice;
+  const int c1 = min(nchunks, c0 + chunks_per_slice);
+  // DMA sources: token row wave*8 + lane/8, router rows (i*8 + wave)*8 + lane/8
+  const int slot = lane & 7;
+  const uint16_t* xsrc;
+  {
+    const int r = wv * 8 + (lane >> 3);
+    int64_t t = t0 + r;
+    t = t < T ? t : T - 1;
+    xsrc = x + t * H + ((slot ^ (r & 7)) * 8);
+  }
+  const uint16_t* wsrc[kWI];
+#pragma unroll
+  for (int i = 0; i < kWI; ++i) {
+    const int r = (i * 8 + wv) * 8 + (lane >> 3);
+    const int e = r < E ? r : E - 1;
+    wsrc[i] = wr + (int64_t)e * H + ((slot ^ (r & 7)) * 8);
+  }
+  auto issue = [&](int stage, int c) {
+    uint8_t* sb = smem + stage * kStage;
+    route_lds_load16(xsrc + c * 64, sb + wv * 1024);
+#pragma unroll
+    for (int i = 0; i < kWI; ++i) route_lds_load16(wsrc[i] + c * 64, sb + kXB + (i * 8 + wv) * 1024);
+  };
+  const int et = wave / kWT, sub = wave % kWT;
+  const int j0 = kWT == 1 ? 0 : (sub & 1);
+  const int u0 = kWT == 4 ? (sub >> 1) : 0;
+  f32x16 acc[kNJ] = {};
+  if (c0 < c1) issue(0, c0);
+  if (c0 + 1 < c1) issue(1, c0 + 1);
+  for (int c = c0; c < c1; ++c) {
+    if (c + 1 < c1) __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+    __syncthreads();   // chunk c landed for all; chunk c-1's stage is free
+    if (c + 2 < c1) issue((c + 2 - c0) % kRouteStages, c + 2);
+    const uint8_t* sb = smem + ((c - c0) % kRouteStages) * kStage;
+#pragma unroll
+    for (int u = u0; u < 4; u += kUStep) {
+      const int q = 2 * u + hl;
+      const bf16x8 a = *(const bf16x8*)(sb + kXB + rswz(et * 32 + l32, q));
+#pragma unroll
+      for (int jj = 0; jj < kNJ; ++jj) {
+        const bf16x8 b = *(const bf16x8*)(sb + rswz((j0 + jj) * 32 + l32, q));
+        acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jj], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();   // the ring is free: reuse it for the logit tile s_l[token][expert]
+  float* s_l = (float*)smem;   // rows of kEP + 1 floats: the tile's lanes hit distinct banks
+  // C[i][n] of a tile: i = expert (r/4)*8 + hl*4 + r%4, n = token l32
+  auto put = [&](bool add) {
+#pragma unroll
+    for (int jj = 0; jj < kNJ; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = (j0 + jj) * 32 + l32, i = et * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+        float* d = s_l + n * (kEP + 1) + i;
+        *d = add ? *d + acc[jj][r] : acc[jj][r];
+      }
+  };
+  if (u0 == 0) put(false);
+  __syncthreads();
+  if (u0 != 0) put(true);   // the other half of the 16-deep slices, added second
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kBigTok * kEP; idx += 512) {
+    const int n = idx / kEP, i = idx - n * kEP;
+    const int64_t t = t0 + n;
+    if (t < T && i < E) part[((int64_t)blockIdx.y * T + t) * E + i] = s_l[n * (kEP + 1) + i];
+  }
+}
+
 // one wave per token: key = sum over slices + bias, then the top-k selection
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int slices, int64_t T,
                                                    int E, const float* __restrict__ bias, int k, int score,
@@ -222,7 +332,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
 
 }  // namespace
 
+// large batches take the LDS-staged router
+bool route_big(int64_t T, int H) { return T >= 256 && H % 64 == 0; }
+
 int route_slices(int64_t T, int H, int E) {
+  if (route_big(T, H)) {
+    const int64_t tiles = (T + kBigTok - 1) / kBigTok;
+    const int nchunks = H / 64;
+    int64_t sl = (256 + tiles - 1) / tiles;
+    const int max_sl = nchunks / 4 > 0 ? nchunks / 4 : 1;   // at least 4 chunks per slice
+    if (sl > max_sl) sl = max_sl;
+    return (int)(sl < 1 ? 1 : sl);
+  }
   const int64_t tiles = ((T + 31) / 32) * ((E + 31) / 32);
   const int max_slices = (H / 16) / 4;   // at least one 16-deep step per wave
   int64_t sl = (512 + tiles - 1) / tiles;
@@ -239,6 +360,22 @@ hipError_t launch_route_topk(const void* x, const void* w_router, const float* b
                              int H, int E, int k, int act_bf16, int score, int renorm,
                              float routed_scale, int32_t* ids, float* w, float* part, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (act_bf16 && route_big(T, H)) {
+    const int slices = route_slices(T, H, E);
+    const int nchunks = H / 64;
+    const int per = (nchunks + slices - 1) / slices;
+    dim3 grid((unsigned)((T + kBigTok - 1) / kBigTok), (unsigned)slices);
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* wb = (const uint16_t*)w_router;
+    if (E <= 64) hipLaunchKernelGGL(logits_lds_kernel<64>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
+    else if (E <= 128) hipLaunchKernelGGL(logits_lds_kernel<128>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
+    else hipLaunchKernelGGL(logits_lds_kernel<256>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, part, slices, T, E, bias,
+                       k, score, renorm, routed_scale, ids, w);
+    return hipGetLastError();
+  }
   if (act_bf16) {
     const int slices = route_slices(T, H, E);
     const int nsteps = H / 16;
