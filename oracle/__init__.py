@@ -81,6 +81,14 @@ def lib():
         L.orc_expert_pairs.restype = None
         L.orc_quant_rows.argtypes = [vp, i32, i64, i32, i32, vp, vp]
         L.orc_quant_rows.restype = None
+        L.orc_bwd_tokens.argtypes = [ctypes.POINTER(_Experts), i64, i32, vp, i32, vp, i32, i32, i32, dbl,
+                                     vp, vp, vp, vp, vp, i64, vp, vp, vp]
+        L.orc_bwd_tokens.restype = None
+        L.orc_bwd_expert_rows.argtypes = [ctypes.POINTER(_Experts), i32, i32, vp, i32, i64, i32, vp, i32,
+                                          vp, vp, vp, vp]
+        L.orc_bwd_expert_rows.restype = None
+        L.orc_bwd_router.argtypes = [i64, i32, i32, vp, i32, vp, vp, vp]
+        L.orc_bwd_router.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
@@ -305,3 +313,84 @@ def forward(x, w_r, bias, experts: Experts, k: int, score: int, renormalize: boo
     counts, offsets, perm, inv = permute(ids, experts.E)
     out = experts.combine(x, ids, w, tokens)
     return ids, w, counts, offsets, perm, inv, out
+
+
+# --------------------------------------------------------------------- backward
+
+def _f64(a):
+    if a is not None and not isinstance(a, np.ndarray):
+        a = a.detach().cpu().double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def bwd_tokens(experts: Experts, x, w_r, score: int, renormalize: bool, routed_scale: float,
+               keys, ids, w, dout, tokens=None):
+    """(dx [n,H], dw [n,k], dkey [n,E]) fp64 for the listed tokens (all by default).
+
+    keys [T,E], ids and w [T,k] come from ``route(..., want_keys=True)``;
+    dout [T,H] is the gradient of the layer output."""
+    xa, xf = _as_host(x)
+    wa, wf = _as_host(w_r)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    keys, w, dout = _f64(keys), _f64(w), _f64(dout)
+    tok = np.arange(T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+    n = tok.size
+    dx = np.empty((n, experts.H), dtype=np.float64)
+    dw = np.empty((n, k), dtype=np.float64)
+    dkey = np.empty((n, experts.E), dtype=np.float64)
+    lib().orc_bwd_tokens(ctypes.byref(experts._st), T, k, _p(xa), xf, _p(wa), wf, int(score),
+                         int(bool(renormalize)), float(routed_scale), _p(keys), _p(ids), _p(w), _p(dout),
+                         _p(tok), n, _p(dx), _p(dw), _p(dkey))
+    return dx, dw, dkey
+
+
+BWD_GATE, BWD_UP, BWD_DOWN = 0, 1, 2
+
+
+def bwd_expert_rows(experts: Experts, which: int, e: int, rows, x, ids, w, dout):
+    """Rows of dW_gate[e] / dW_up[e] ([I,H]) or dW_down[e] ([H,I]) as fp64 [n, cols]."""
+    xa, xf = _as_host(x)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    w, dout = _f64(w), _f64(dout)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = experts.I if which == BWD_DOWN else experts.H
+    out = np.empty((rows.size, cols), dtype=np.float64)
+    lib().orc_bwd_expert_rows(ctypes.byref(experts._st), int(which), int(e), _p(rows), rows.size, T, k,
+                              _p(xa), xf, _p(ids), _p(w), _p(dout), _p(out))
+    return out
+
+
+def bwd_router(x, dkey):
+    """(dW_r [E,H], dbias [E]) fp64 from dkey [T,E]."""
+    xa, xf = _as_host(x)
+    dkey = _f64(dkey)
+    T, E = dkey.shape
+    H = xa.shape[1]
+    dwr = np.empty((E, H), dtype=np.float64)
+    db = np.empty(E, dtype=np.float64)
+    lib().orc_bwd_router(T, H, E, _p(xa), xf, _p(dkey), _p(dwr), _p(db))
+    return dwr, db
+
+
+def backward(x, w_r, bias, experts: Experts, k: int, score: int, renormalize: bool, routed_scale: float,
+             dout):
+    """Every gradient of the layer for the output gradient dout [T,H], as a dict of
+    fp64 arrays: dx, dw_router, dbias, dw_gate, dw_up, dw_down, plus ids, w, dw
+    (gradient of the routing weights) and dkey."""
+    ids, w, keys = route(x, w_r, bias, k, score, renormalize, routed_scale, want_keys=True)
+    dx, dw, dkey = bwd_tokens(experts, x, w_r, score, renormalize, routed_scale, keys, ids, w, dout)
+    dwr, db = bwd_router(x, dkey)
+    E, I, H = experts.E, experts.I, experts.H
+    dwg = np.zeros((E, I, H))
+    dwu = np.zeros((E, I, H))
+    dwd = np.zeros((E, H, I))
+    for e in range(E):
+        if not (ids == e).any():
+            continue
+        dwg[e] = bwd_expert_rows(experts, BWD_GATE, e, np.arange(I), x, ids, w, dout)
+        dwu[e] = bwd_expert_rows(experts, BWD_UP, e, np.arange(I), x, ids, w, dout)
+        dwd[e] = bwd_expert_rows(experts, BWD_DOWN, e, np.arange(H), x, ids, w, dout)
+    return dict(ids=ids, w=w, keys=keys, dw=dw, dkey=dkey, dx=dx, dw_router=dwr, dbias=db,
+                dw_gate=dwg, dw_up=dwu, dw_down=dwd)

@@ -43,9 +43,16 @@
  *     one UE8M0 scale per row per 32 consecutive K (the OCP MX block; the page
  *     gives no FP4 block size); activations as for FP8 (e4m3, per row per 128).
  *
+ * Backward (section "SonicMoE": training of the gated-MLP experts): the
+ * gradients of every input and parameter for a given output gradient, with the
+ * top-k selection held fixed (orc_bwd_tokens, orc_bwd_expert_rows,
+ * orc_bwd_router; formulas in the comment above them).
+ *
  * Pins: every function here is checked by the CPU tests against closed forms,
  * library routines on special cases, brute force on tiny inputs and a worked
- * example computed by hand (tests/golden).  No function is "parity unpinned".
+ * example computed by hand (tests/golden); the backward against central finite
+ * differences of this file's forward and a dense autograd formulation.  No
+ * function is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -419,6 +426,235 @@ void orc_quant_rows(const void *x, int xdt, int64_t rows, int n, int group,
         }
         free(v);
         free(d);
+    }
+}
+
+/* ------------------------------------------------------------------ backward */
+
+/* Backward of the layer ("Experts backends", section "SonicMoE": the page
+ * names training of the gated-MLP experts as SonicMoE's focus; the gradient
+ * formulas are those of the forward above differentiated by hand).  Given the
+ * gradient dout[T,H] of the output, with the selection ids held fixed (the
+ * top-k choice is piecewise constant in the inputs):
+ *   dw[t,i]  = dout_t . y(t,i)                         (routing weight)
+ *   dy       = w[t,i] dout_t,  da = W_down^T dy
+ *   dg       = da * u * act'(g),  du = da * act(g)
+ *   dx_t     = sum_i (W_gate^T dg + W_up^T du) + sum_e dkey[t,e] W_r[e]
+ *   dW_down[e] = sum over the pairs of e of dy a^T, dW_gate[e] = sum dg x^T,
+ *   dW_up[e] = sum du x^T,  dW_r = dkey^T x,  dbias = sum_t dkey[t,:]
+ * where dkey is the gradient of the router key through the score function,
+ * the renormalisation and the routed scale.  Experts in F32 or BF16 only (no
+ * quantizer in the backward). */
+
+/* derivative of the gate activation */
+static double gate_act_deriv(int gate, double g)
+{
+    if (gate == ORC_GATE_GELU) {
+        double Phi = 0.5 * (1.0 + erf(g / sqrt(2.0)));
+        double phi = exp(-0.5 * g * g) / sqrt(2.0 * 3.14159265358979323846);
+        return Phi + g * phi;
+    }
+    if (gate == ORC_GATE_RELU) return g > 0.0 ? 1.0 : 0.0;
+    double sg = 1.0 / (1.0 + exp(-g));
+    return sg * (1.0 + g * (1.0 - sg));
+}
+
+/* g, u and a = act(g) * u of expert e on the fp64 row xr */
+static void expert_gua(const orc_experts *W, int e, const double *xr, double *g, double *u, double *a)
+{
+    int H = W->H, I = W->I;
+    for (int j = 0; j < I; ++j) {
+        double gj = 0.0, uj = 0.0;
+        for (int h = 0; h < H; ++h) {
+            gj += xr[h] * weight(W, W->w_gate, W->s_gate, e, j, h, I, H);
+            uj += xr[h] * weight(W, W->w_up, W->s_up, e, j, h, I, H);
+        }
+        g[j] = gj;
+        u[j] = uj;
+        a[j] = gate_act(W->gate, gj) * uj;
+    }
+}
+
+/* da = W_down[e]^T dy */
+static void down_transpose(const orc_experts *W, int e, const double *dy, double *da)
+{
+    int H = W->H, I = W->I;
+    for (int j = 0; j < I; ++j) {
+        double s = 0.0;
+        for (int o = 0; o < H; ++o) s += dy[o] * weight(W, W->w_down, W->s_down, e, o, j, H, I);
+        da[j] = s;
+    }
+}
+
+/* Token-side gradients for a list of tokens.  keys [T,E] are the router keys
+ * (logits plus bias), ids and w [T,k] the selection and routing weights of the
+ * forward; dout [T,H] fp64.  Out, per listed token n: dx [n,H], dw [n,k],
+ * dkey [n,E] (any may be NULL except dx). */
+void orc_bwd_tokens(const orc_experts *W, int64_t T, int k, const void *x, int xdt,
+                    const void *w_r, int wdt, int score, int renormalize, double routed_scale,
+                    const double *keys, const int32_t *ids, const double *w, const double *dout,
+                    const int64_t *tokens, int64_t ntok, double *dx, double *dw_out, double *dkey_out)
+{
+    int H = W->H, I = W->I, E = W->E;
+    int64_t n;
+    (void)T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (n = 0; n < ntok; ++n) {
+        int64_t t = tokens[n];
+        double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        double *da = (double *)malloc(sizeof(double) * (size_t)I);
+        double *dy = (double *)malloc(sizeof(double) * (size_t)H);
+        double *dwt = (double *)malloc(sizeof(double) * (size_t)k);
+        double *s = (double *)malloc(sizeof(double) * (size_t)E);
+        double *ds = (double *)calloc((size_t)E, sizeof(double));
+        double *dkey = (double *)malloc(sizeof(double) * (size_t)E);
+        double *dxr = dx + n * H;
+        const double *dot = dout + t * H;
+        for (int h = 0; h < H; ++h) {
+            xr[h] = decode_elem(x, xdt, t * H + h);
+            dxr[h] = 0.0;
+        }
+        for (int i = 0; i < k; ++i) {
+            int e = ids[t * k + i];
+            double wi = w[t * k + i];
+            expert_gua(W, e, xr, g, u, a);
+            /* dw = dout . y with y = W_down a */
+            double d = 0.0;
+            for (int o = 0; o < H; ++o) {
+                double yo = 0.0;
+                for (int j = 0; j < I; ++j) yo += a[j] * weight(W, W->w_down, W->s_down, e, o, j, H, I);
+                d += dot[o] * yo;
+            }
+            dwt[i] = d;
+            for (int o = 0; o < H; ++o) dy[o] = wi * dot[o];
+            down_transpose(W, e, dy, da);
+            for (int j = 0; j < I; ++j) {
+                double dg = da[j] * u[j] * gate_act_deriv(W->gate, g[j]);
+                double du = da[j] * gate_act(W->gate, g[j]);
+                for (int h = 0; h < H; ++h)
+                    dxr[h] += dg * weight(W, W->w_gate, W->s_gate, e, j, h, I, H) +
+                              du * weight(W, W->w_up, W->s_up, e, j, h, I, H);
+            }
+        }
+        /* scores of all experts (softmax over all E, or sigmoid) */
+        const double *key = keys + t * E;
+        if (score == ORC_SOFTMAX) {
+            double m = key[0], den = 0.0;
+            for (int e = 1; e < E; ++e) if (key[e] > m) m = key[e];
+            for (int e = 0; e < E; ++e) den += exp(key[e] - m);
+            for (int e = 0; e < E; ++e) s[e] = exp(key[e] - m) / den;
+        } else {
+            for (int e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + exp(-key[e]));
+        }
+        /* through the routed scale and the renormalisation: w_i = c s_i / S */
+        double S = 0.0, dws = 0.0;
+        for (int i = 0; i < k; ++i) {
+            S += s[ids[t * k + i]];
+            dws += dwt[i] * s[ids[t * k + i]];
+        }
+        for (int i = 0; i < k; ++i) {
+            int e = ids[t * k + i];
+            ds[e] = renormalize ? routed_scale * (dwt[i] / S - dws / (S * S)) : routed_scale * dwt[i];
+        }
+        /* through the score function */
+        if (score == ORC_SOFTMAX) {
+            double sds = 0.0;
+            for (int e = 0; e < E; ++e) sds += s[e] * ds[e];
+            for (int e = 0; e < E; ++e) dkey[e] = s[e] * (ds[e] - sds);
+        } else {
+            for (int e = 0; e < E; ++e) dkey[e] = ds[e] * s[e] * (1.0 - s[e]);
+        }
+        for (int e = 0; e < E; ++e)
+            for (int h = 0; h < H; ++h) dxr[h] += dkey[e] * decode_elem(w_r, wdt, (int64_t)e * H + h);
+        if (dw_out) memcpy(dw_out + n * k, dwt, sizeof(double) * (size_t)k);
+        if (dkey_out) memcpy(dkey_out + n * E, dkey, sizeof(double) * (size_t)E);
+        free(xr); free(g); free(u); free(a); free(da); free(dy); free(dwt); free(s); free(ds); free(dkey);
+    }
+}
+
+/* Rows of one expert's weight gradient, summed over that expert's (token,
+ * slot) pairs in token-major order.  which: 0 dW_gate [I,H], 1 dW_up [I,H],
+ * 2 dW_down [H,I]; rows [nrows] are row indices of that matrix; out
+ * [nrows, cols] fp64.  The per-pair vectors (a, or dg / du) are computed
+ * first, then each requested row is a sum of outer-product rows. */
+void orc_bwd_expert_rows(const orc_experts *W, int which, int e, const int32_t *rows, int nrows,
+                         int64_t T, int k, const void *x, int xdt, const int32_t *ids, const double *w,
+                         const double *dout, double *out)
+{
+    int H = W->H, I = W->I;
+    int cols = which == 2 ? I : H;
+    int64_t np_ = 0, q;
+    int r;
+    for (int64_t p = 0; p < T * k; ++p) np_ += ids[p] == e;
+    int64_t *pairs = (int64_t *)malloc(sizeof(int64_t) * (size_t)(np_ + 1));
+    np_ = 0;
+    for (int64_t p = 0; p < T * k; ++p) if (ids[p] == e) pairs[np_++] = p;
+    /* per pair: a (down) or the channel gradient d = dg or du (gate / up), [np_, I] */
+    double *vec = (double *)malloc(sizeof(double) * (size_t)(np_ * I + 1));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (q = 0; q < np_; ++q) {
+        int64_t t = pairs[q] / k;
+        double wi = w[pairs[q]];
+        double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        double *dy = (double *)malloc(sizeof(double) * (size_t)H);
+        double *da = (double *)malloc(sizeof(double) * (size_t)I);
+        double *v = vec + q * I;
+        for (int h = 0; h < H; ++h) xr[h] = decode_elem(x, xdt, t * H + h);
+        expert_gua(W, e, xr, g, u, a);
+        if (which == 2) {
+            memcpy(v, a, sizeof(double) * (size_t)I);
+        } else {
+            for (int o = 0; o < H; ++o) dy[o] = wi * dout[t * H + o];
+            down_transpose(W, e, dy, da);
+            for (int j = 0; j < I; ++j)
+                v[j] = which == 0 ? da[j] * u[j] * gate_act_deriv(W->gate, g[j]) : da[j] * gate_act(W->gate, g[j]);
+        }
+        free(xr); free(g); free(u); free(a); free(dy); free(da);
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (r = 0; r < nrows; ++r) {
+        double *orow = out + (int64_t)r * cols;
+        int row = rows[r];
+        for (int c = 0; c < cols; ++c) orow[c] = 0.0;
+        for (int64_t q2 = 0; q2 < np_; ++q2) {
+            int64_t t = pairs[q2] / k;
+            if (which == 2) {
+                /* dW_down[o, :] += dy[o] a with dy = w dout_t */
+                double dyo = w[pairs[q2]] * dout[t * H + row];
+                for (int j = 0; j < I; ++j) orow[j] += dyo * vec[q2 * I + j];
+            } else {
+                /* dW_gate[j, :] += dg[j] x_t  (dW_up: du[j] x_t) */
+                double d = vec[q2 * I + row];
+                for (int h = 0; h < H; ++h) orow[h] += d * decode_elem(x, xdt, t * H + h);
+            }
+        }
+    }
+    free(pairs);
+    free(vec);
+}
+
+/* Router parameter gradients from dkey [T,E]: dW_r [E,H] = dkey^T x and
+ * dbias [E] = column sums of dkey, both summed in token order. */
+void orc_bwd_router(int64_t T, int H, int E, const void *x, int xdt, const double *dkey,
+                    double *dwr, double *dbias)
+{
+    int e;
+#pragma omp parallel for schedule(static)
+    for (e = 0; e < E; ++e) {
+        double b = 0.0;
+        for (int h = 0; h < H; ++h) dwr[(int64_t)e * H + h] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            double d = dkey[t * E + e];
+            b += d;
+            for (int h = 0; h < H; ++h) dwr[(int64_t)e * H + h] += d * decode_elem(x, xdt, t * H + h);
+        }
+        dbias[e] = b;
     }
 }
 
