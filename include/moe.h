@@ -109,7 +109,7 @@ typedef enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1 } moe_pack_which;
 
 typedef enum {
     MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GATE_UP = 2, MOE_OP_DOWN = 3,
-    MOE_OP_COMBINE = 4, MOE_OP_FORWARD = 5
+    MOE_OP_COMBINE = 4, MOE_OP_FORWARD = 5, MOE_OP_BACKWARD = 6
 } moe_op;
 
 /* Layer description (host memory, read during the call only). */
@@ -237,6 +237,43 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Backward of the whole layer ("Experts backends", section "SonicMoE": the
+ * backend built for training gated-MLP experts).  Every gradient of the layer
+ * for the output gradient d_out, with the top-k selection held fixed (it is
+ * piecewise constant in the inputs):
+ *   dw[t,i]     = d_out[t] . y(t,i)                    (routing-weight gradient)
+ *   dy          = w[t,i] d_out[t],  da = W_down[e]^T dy
+ *   dg          = da * u * act'(g),  du = da * act(g)   (act = desc->gate_act)
+ *   dx[t]       = sum_i (W_gate[e]^T dg + W_up[e]^T du) + sum_e dkey[t,e] w_router[e]
+ *   dw_gate[e]  = sum over the pairs of e of dg x^T, dw_up[e] = sum du x^T,
+ *   dw_down[e]  = sum dy a^T (a = act(g) * u),
+ *   dw_router   = dkey^T x,  d_bias = sum_t dkey[t,:]
+ * where dkey is the gradient of the router key through the routed scale, the
+ * renormalisation (if any) and the score (softmax over all E, or sigmoid).
+ * Nothing of the forward is kept: routing, permutation and g, u are
+ * recomputed from x and the weights (selection and routing weights come out
+ * bitwise identical to moe_forward's).
+ *   x, w_router, router_bias, w_gate, w_up, w_down  as for moe_forward (bf16
+ *                 activations and bf16 row-major experts only)
+ *   d_out         [T,H] bf16 in
+ *   dx            [T,H] bf16 out
+ *   dw_router     [E,H] bf16 out
+ *   d_bias        [E] fp32 out, or NULL (not computed)
+ *   dw_gate, dw_up [E,I,H] and dw_down [E,H,I] bf16 out (experts that no token
+ *                 selected get zeros)
+ *   ws, ws_bytes  workspace of moe_workspace_bytes(desc, MOE_OP_BACKWARD)
+ * Products accumulate in fp32 (bf16 MFMA); g, u and W_down^T d_out stay
+ * fp32, the gated-activation gradients and the scaled activations (inputs of
+ * the next GEMMs) are rounded to bf16.
+ * No atomics: results are bitwise reproducible.  T = 0 writes zero parameter
+ * gradients (no workspace needed).  MOE_EUNSUPPORTED for fp32,
+ * FP8 or FP4 experts, packed weights, or H, I not multiples of 128. */
+moe_status moe_backward(const moe_desc* desc, const void* x, const void* w_router,
+                        const float* router_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* d_out, void* dx, void* dw_router,
+                        float* d_bias, void* dw_gate, void* dw_up, void* dw_down,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of the packed copy of one weight set (MOE_PACK_GATE_UP: w_gate and
  * w_up together; MOE_PACK_DOWN: w_down) for desc's shapes and weight dtype;
  * 0 if the description is invalid or uses fp32 weights. */
@@ -265,8 +302,8 @@ const char* moe_status_str(int status);
 const char* moe_last_error(void);
 
 /* ------------------------------------------------------------------------ */
-/* Stage timing, for measurement.  While enabled, moe_forward brackets each of
- * its kernels with HIP events on the caller's stream.  moe_timing_read waits
+/* Stage timing, for measurement.  While enabled, moe_forward and moe_backward
+ * bracket each of their kernels with HIP events on the caller's stream.  moe_timing_read waits
  * for the recorded events, adds their elapsed times into ms[stage] and the
  * number of timed launches into launches[stage] (both host arrays of
  * MOE_NUM_STAGES entries), and clears the record.  Not thread-safe.
@@ -276,7 +313,12 @@ const char* moe_last_error(void);
 enum {
     MOE_STAGE_ROUTE = 0, MOE_STAGE_HIST = 1, MOE_STAGE_SCAN = 2, MOE_STAGE_SCATTER = 3,
     MOE_STAGE_QUANT_X = 4, MOE_STAGE_GATE_UP = 5, MOE_STAGE_DOWN = 6, MOE_STAGE_COMBINE = 7,
-    MOE_NUM_STAGES = 8
+    /* moe_backward: recompute of g and u; the two data-gradient GEMMs; the
+     * weight-gradient GEMMs; the router's gradients; gathers, the
+     * gated-activation gradient and the dx sum */
+    MOE_STAGE_BWD_RECOMPUTE = 8, MOE_STAGE_BWD_DATA = 9, MOE_STAGE_BWD_WEIGHT = 10,
+    MOE_STAGE_BWD_ROUTER = 11, MOE_STAGE_BWD_MISC = 12,
+    MOE_NUM_STAGES = 13
 };
 moe_status moe_timing_enable(int on);
 moe_status moe_timing_read(double* ms, int64_t* launches);

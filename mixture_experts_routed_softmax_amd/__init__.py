@@ -41,8 +41,9 @@ MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = range(2)
 MOE_GATE_SILU, MOE_GATE_GELU, MOE_GATE_RELU = range(3)
 MOE_PACK_GATE_UP, MOE_PACK_DOWN = range(2)
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GATE_UP, MOE_OP_DOWN, MOE_OP_COMBINE,
- MOE_OP_FORWARD) = range(6)
-STAGES = ("route", "hist", "scan", "scatter", "quant_x", "gate_up", "down", "combine")
+ MOE_OP_FORWARD, MOE_OP_BACKWARD) = range(7)
+STAGES = ("route", "hist", "scan", "scatter", "quant_x", "gate_up", "down", "combine",
+          "bwd_recompute", "bwd_data", "bwd_weight", "bwd_router", "bwd_misc")
 MOE_NUM_STAGES = len(STAGES)
 
 
@@ -75,6 +76,8 @@ _sigs = {
     "moe_unpermute_combine": [_DP, _vp, _vp, _vp, _vp, _vp],
     "moe_forward": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                     ctypes.c_size_t, _vp],
+    "moe_backward": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                     ctypes.c_size_t, _vp],
 }
 for _name, _args in _sigs.items():
     getattr(_lib, _name).argtypes = _args
@@ -234,6 +237,14 @@ def moe_forward(desc, x, w_router, router_bias, w_gate, w_up, w_down, w_gate_sca
                             _ptr(w_up_scales), _ptr(w_down_scales), _ptr(out), _ptr(topk_ids_out),
                             _ptr(topk_w_out), _ptr(counts_out), _ptr(ws), _nbytes(ws),
                             _stream(stream)))
+
+
+def moe_backward(desc, x, w_router, router_bias, w_gate, w_up, w_down, d_out, dx, dw_router, d_bias,
+                 dw_gate, dw_up, dw_down, ws=None, stream=None):
+    _check(_lib.moe_backward(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate),
+                             _ptr(w_up), _ptr(w_down), _ptr(d_out), _ptr(dx), _ptr(dw_router), _ptr(d_bias),
+                             _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws),
+                             _stream(stream)))
 
 
 def moe_timing_enable(on: bool):

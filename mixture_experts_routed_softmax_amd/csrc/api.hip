@@ -261,6 +261,8 @@ ForwardWs carve_forward(Carve& c, const moe_desc* d) {
   return w;
 }
 
+size_t backward_ws_size(const moe_desc* d);
+
 size_t ws_size(const moe_desc* d, int op) {
   Carve c{nullptr};
   switch (op) {
@@ -276,6 +278,7 @@ size_t ws_size(const moe_desc* d, int op) {
                                             align_up(stream_partial_bytes(d));
     case MOE_OP_COMBINE: return 0;
     case MOE_OP_FORWARD: carve_forward(c, d); return c.off;
+    case MOE_OP_BACKWARD: return backward_ws_size(d);
     default: return 0;
   }
 }
@@ -437,6 +440,100 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   else e = launch_down_fp8(a, grid, st);
   MOE_TRY_HIP(e, "down launch");
   return MOE_OK;
+}
+
+
+// ---- backward ------------------------------------------------------------
+
+moe_status validate_backward(const moe_desc* d) {
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  if (d->act_dtype != MOE_DT_BF16 || d->w_dtype != MOE_DT_BF16)
+    return fail(MOE_EUNSUPPORTED, "the backward takes bf16 activations and bf16 experts");
+  if (d->w_layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_EUNSUPPORTED, "the backward takes row-major weights");
+  if (d->H % 128 || d->I % 128)
+    return fail(MOE_EUNSUPPORTED, "the backward needs H and I multiples of 128 (H = %d, I = %d)", d->H, d->I);
+  return MOE_OK;
+}
+
+// the description the backward's grouped GEMMs are planned with
+moe_desc backward_desc(const moe_desc* d) {
+  moe_desc b = *d;
+  b.path = MOE_PATH_GROUPED;
+  b.w_layout = MOE_LAYOUT_ROWMAJOR;
+  return b;
+}
+
+int expert_pad(int E) { return (E + 127) / 128 * 128; }
+
+struct BackwardWs {
+  float* route_part;
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  PermuteWs pw;
+  int32_t* perm;
+  int32_t* inv;
+  int32_t* touched;
+  Schedule* sched_gu;   // recompute of g, u
+  Schedule* sched_e;    // e = W_down^T dout (channel tiles of I)
+  Schedule* sched_dx;   // dx rows (channel tiles of H)
+  uint16_t* x_sorted;
+  uint16_t* dout_sorted;
+  float* gu;
+  float* ev;
+  uint16_t* ap;
+  uint16_t* dgu;
+  float* dw;
+  float* dxp;
+  float* dkey;
+  uint16_t* dkey_b;
+  float* dxr;
+  uint16_t* zeros;
+};
+
+BackwardWs carve_backward(Carve& c, const moe_desc* d0) {
+  const moe_desc bd = backward_desc(d0);
+  const moe_desc* d = &bd;
+  const int64_t P = pairs(d);
+  const int64_t H = d->H, I = d->I;
+  BackwardWs w{};
+  w.route_part = (float*)c.take<uint8_t>(route_workspace_bytes(d->T, d->H, d->E, 1));
+  w.ids = c.take<int32_t>(P);
+  w.w = c.take<float>(P);
+  w.counts = c.take<int32_t>(d->E);
+  w.offsets = c.take<int32_t>(d->E + 1);
+  w.pw = carve_permute(c, d, false);
+  w.perm = c.take<int32_t>(P);
+  w.inv = c.take<int32_t>(P);
+  w.touched = c.take<int32_t>(d->E + 1);
+  w.sched_gu = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
+  w.sched_e = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, d->I / 128)));
+  w.sched_dx = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, d->H / 128)));
+  w.x_sorted = c.take<uint16_t>((size_t)P * H);
+  w.dout_sorted = c.take<uint16_t>((size_t)P * H);
+  w.gu = c.take<float>((size_t)P * 2 * I);
+  w.ev = c.take<float>((size_t)P * I);
+  w.ap = c.take<uint16_t>((size_t)P * I);
+  w.dgu = c.take<uint16_t>((size_t)P * 2 * I);
+  w.dw = c.take<float>(P);
+  w.dxp = c.take<float>((size_t)P * H);
+  w.dkey = c.take<float>((size_t)d->T * d->E);
+  w.dkey_b = c.take<uint16_t>((size_t)d->T * expert_pad(d->E));
+  w.dxr = c.take<float>((size_t)d->T * H);
+  w.zeros = c.take<uint16_t>(128);
+  return w;
+}
+
+size_t backward_ws_size(const moe_desc* d) {
+  const std::string keep = g_err;
+  const bool ok = validate_backward(d) == MOE_OK;
+  g_err = keep;
+  if (!ok || d->T == 0) return 0;
+  Carve c{nullptr};
+  carve_backward(c, d);
+  return c.off;
 }
 
 }  // namespace
@@ -633,6 +730,191 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
     MOE_TRY_HIP(launch_combine(fw.y, d->y_dtype == MOE_DT_F32, fw.inv, w, d->T, d->k, d->H, out,
                                d->act_dtype == MOE_DT_F32, st),
                 "combine launch");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router, const float* bias,
+                        const void* w_gate, const void* w_up, const void* w_down, const void* d_out, void* dx,
+                        void* dw_router, float* d_bias, void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                        size_t ws_bytes, void* stream) {
+  g_err.clear();
+  moe_status s = validate_backward(d0);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (d0->T == 0) {
+    // no token: every parameter gradient is zero
+    if (!dw_router || !dw_gate || !dw_up || !dw_down) return fail(MOE_EINVAL, "NULL gradient output");
+    const int64_t HI = (int64_t)d0->H * d0->I * d0->E * 2;
+    MOE_TRY_HIP(launch_fill_zero(dw_gate, HI, st), "zero-fill launch");
+    MOE_TRY_HIP(launch_fill_zero(dw_up, HI, st), "zero-fill launch");
+    MOE_TRY_HIP(launch_fill_zero(dw_down, HI, st), "zero-fill launch");
+    MOE_TRY_HIP(launch_fill_zero(dw_router, (int64_t)d0->E * d0->H * 2, st), "zero-fill launch");
+    if (d_bias) MOE_TRY_HIP(launch_fill_zero(d_bias, (int64_t)d0->E * 4, st), "zero-fill launch");
+    return MOE_OK;
+  }
+  if ((s = check_ws(d0, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return s;
+  const void* ptrs[] = {x, w_router, w_gate, w_up, w_down, d_out, dx, dw_router, dw_gate, dw_up, dw_down};
+  for (const void* p : ptrs) {
+    if (!p) return fail(MOE_EINVAL, "NULL tensor argument");
+    if (!aligned16(p)) return fail(MOE_EINVAL, "tensors must be 16-byte aligned");
+  }
+  const moe_desc bd = backward_desc(d0);
+  const moe_desc* d = &bd;
+  Carve c{(uint8_t*)ws};
+  BackwardWs bw = carve_backward(c, d);
+  const int64_t P = pairs(d);
+  const int H = d->H, I = d->I, E = d->E, Epad = expert_pad(d->E);
+
+  MOE_TRY_HIP(launch_fill_zero(bw.zeros, 256, st), "zero-fill launch");
+  {
+    StageTimer tm(MOE_STAGE_ROUTE, st);
+    MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, H, E, d->k, 1, d->score, d->renormalize,
+                                  d->routed_scale, bw.ids, bw.w, bw.route_part, st),
+                "router launch");
+  }
+  const SchedRequest sgu = sched_req(bw.sched_gu, d, gate_up_ntiles(d));
+  const SchedRequest se = sched_req(bw.sched_e, d, I / 128);
+  const SchedRequest sdx = sched_req(bw.sched_dx, d, H / 128);
+  if ((s = run_permute(d, bw.ids, bw.counts, bw.offsets, bw.perm, bw.inv, bw.touched, bw.pw, sgu, se, st)) != MOE_OK)
+    return s;
+  {
+    StageTimer tm(MOE_STAGE_BWD_MISC, st);
+    MOE_TRY_HIP(launch_schedule(bw.offsets, E, sdx, st), "schedule launch");
+    MOE_TRY_HIP(launch_gather_rows(x, bw.perm, d->k, P, (int64_t)H * 2, bw.x_sorted, st), "gather launch");
+    MOE_TRY_HIP(launch_gather_rows(d_out, bw.perm, d->k, P, (int64_t)H * 2, bw.dout_sorted, st), "gather launch");
+  }
+  {
+    // g and u of every sorted row, recomputed
+    StageTimer tm(MOE_STAGE_BWD_RECOMPUTE, st);
+    GemmArgs a = gemm_common(d);
+    a.act = bw.x_sorted;
+    a.w0 = w_gate;
+    a.w1 = w_up;
+    a.K = H;
+    a.N = I;
+    a.out = bw.gu;
+    a.gu_out = 1;
+    a.sched = bw.sched_gu;
+    a.offsets = bw.offsets;
+    MOE_TRY_HIP(launch_gate_up_bf16(a, grid_for(sgu.capacity), st), "gate/up recompute launch");
+  }
+  {
+    // e = W_down^T dout per sorted row
+    StageTimer tm(MOE_STAGE_BWD_DATA, st);
+    BwdGemmArgs g{};
+    g.a = (const uint16_t*)w_down;
+    g.lda = I;
+    g.a_gs = (int64_t)H * I;
+    g.a_split = g.a_krows = H;
+    g.b = bw.dout_sorted;
+    g.ldb = H;
+    g.zeros = bw.zeros;
+    g.M = I;
+    g.K = H;
+    g.sched = bw.sched_e;
+    g.out = bw.ev;
+    g.ldo = I;
+    g.out_f32 = 1;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, grid_for(se.capacity), st), "backward GEMM launch");
+  }
+  {
+    StageTimer tm(MOE_STAGE_BWD_MISC, st);
+    MOE_TRY_HIP(launch_swiglu_bwd(bw.ev, bw.gu, bw.perm, bw.w, P, I, d->gate_act, bw.dw, bw.ap, bw.dgu, st),
+                "gated-activation backward launch");
+  }
+  {
+    // dx of every sorted row: [dg | du] . [W_gate ; W_up]
+    StageTimer tm(MOE_STAGE_BWD_DATA, st);
+    BwdGemmArgs g{};
+    g.a = (const uint16_t*)w_gate;
+    g.a2 = (const uint16_t*)w_up;
+    g.lda = H;
+    g.a_gs = (int64_t)I * H;
+    g.a_split = I;
+    g.a_krows = 2 * I;
+    g.b = bw.dgu;
+    g.ldb = 2 * I;
+    g.zeros = bw.zeros;
+    g.M = H;
+    g.K = 2 * I;
+    g.sched = bw.sched_dx;
+    g.out = bw.dxp;
+    g.ldo = H;
+    g.out_f32 = 1;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, grid_for(sdx.capacity), st), "backward GEMM launch");
+  }
+  {
+    // dW_down[e] = sum over the expert's rows of dout (w a)^T
+    StageTimer tm(MOE_STAGE_BWD_WEIGHT, st);
+    BwdGemmArgs g{};
+    g.a = bw.ap;
+    g.lda = I;
+    g.b = bw.dout_sorted;
+    g.ldb = H;
+    g.zeros = bw.zeros;
+    g.M = I;
+    g.n_total = g.n_valid = H;
+    g.offsets = bw.offsets;
+    g.out = dw_down;
+    g.ldo = I;
+    g.o_gs = (int64_t)H * I;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * (I / 128) * (H / 128), st), "backward GEMM launch");
+    // dW_gate[e], dW_up[e] = sum over the expert's rows of [dg | du] x^T
+    g = BwdGemmArgs{};
+    g.a = bw.x_sorted;
+    g.lda = H;
+    g.b = bw.dgu;
+    g.ldb = 2 * I;
+    g.zeros = bw.zeros;
+    g.M = H;
+    g.n_total = g.n_valid = 2 * I;
+    g.offsets = bw.offsets;
+    g.out = dw_gate;
+    g.out2 = dw_up;
+    g.n_split = I;
+    g.ldo = H;
+    g.o_gs = (int64_t)I * H;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * (H / 128) * (2 * I / 128), st), "backward GEMM launch");
+  }
+  {
+    // router: key gradients, dW_r = dkey^T x, dbias, and dkey . W_r into dx
+    StageTimer tm(MOE_STAGE_BWD_ROUTER, st);
+    MOE_TRY_HIP(launch_router_bwd(bw.route_part, route_slices(d->T, H, E), d->T, E, Epad, bias, bw.ids, bw.dw,
+                                  d->k, d->score, d->renormalize, d->routed_scale, bw.dkey, bw.dkey_b, st),
+                "router backward launch");
+    if (d_bias) MOE_TRY_HIP(launch_bias_grad(bw.dkey, d->T, E, d_bias, st), "bias gradient launch");
+    BwdGemmArgs g{};
+    g.a = (const uint16_t*)x;
+    g.lda = H;
+    g.b = bw.dkey_b;
+    g.ldb = Epad;
+    g.zeros = bw.zeros;
+    g.M = H;
+    g.K = (int)d->T;
+    g.n_total = Epad;
+    g.n_valid = E;
+    g.out = dw_router;
+    g.ldo = H;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, (H / 128) * (Epad / 128), st), "backward GEMM launch");
+    g = BwdGemmArgs{};
+    g.a = (const uint16_t*)w_router;
+    g.lda = H;
+    g.a_split = g.a_krows = E;
+    g.b = bw.dkey_b;
+    g.ldb = Epad;
+    g.zeros = bw.zeros;
+    g.M = H;
+    g.K = Epad;
+    g.n_total = (int)d->T;
+    g.out = bw.dxr;
+    g.ldo = H;
+    g.out_f32 = 1;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, (int)((d->T + 127) / 128) * (H / 128), st), "backward GEMM launch");
+  }
+  {
+    StageTimer tm(MOE_STAGE_BWD_MISC, st);
+    MOE_TRY_HIP(launch_dx_combine(bw.dxp, bw.dxr, bw.inv, d->T, d->k, H, (uint16_t*)dx, st), "dx combine launch");
   }
   return MOE_OK;
 }

@@ -213,7 +213,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int row = it.row_begin + j * 32 + l32;
     if (j >= ntok || row >= it.row_end) continue;
-    if (kMode == 0) {
+    if (kMode == 0 && a.gu_out) {
+      // g and u themselves in fp32 (the backward recomputes them): [P, 2N], g first
+      float* h = (float*)a.out + (int64_t)row * 2 * N;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = it.ntile * kGemmGateUpChannelsBf16 + wave * 32 + q * 8 + hl * 4;
+        if (ch >= N) continue;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x16& c = acc[t][j];
+          *(f32x4*)(h + t * N + ch) = f32x4{c[q * 4 + 0], c[q * 4 + 1], c[q * 4 + 2], c[q * 4 + 3]};
+        }
+      }
+    } else if (kMode == 0) {
       uint16_t* h = (uint16_t*)a.out + (int64_t)row * N;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

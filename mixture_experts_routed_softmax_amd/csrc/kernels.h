@@ -78,6 +78,7 @@ struct GemmArgs {
   int wtiles;               // packed weights: row tiles per expert
   float* partial;           // weight streaming: split-K partial tiles
   int gate_act;             // moe_gate_act of the gate/up epilogue
+  int gu_out;               // row-major bf16 gate/up: store g and u (fp32 [P, 2N]) instead of h
 };
 
 // tile geometry of the grouped GEMMs
@@ -126,6 +127,50 @@ int64_t packed_tiles(int which_gate_up, int N);
 hipError_t launch_pack(const void* w0, const void* w1, int gate_up, int E, int N, int64_t row_bytes,
                        void* dst, hipStream_t stream);
 hipError_t launch_down_f32(const GemmArgs& a, hipStream_t stream);
+
+// ---- backward (gemm_bwd.hip)
+// C[n][m] = sum_k A[m][k] B[n][k], stored out[n][m].  A is MN-major (K index
+// = memory row).  ragged N: B K-major token rows [row_begin, row_end) of a
+// schedule item (or of 128-row tiles over n_total when sched is null), A rows
+// k < a_split from a + e*a_gs, a_split <= k < a_krows from a2 + e*a_gs,
+// zeros past a_krows; K = a.K.  ragged K: A and B MN-major, K rows
+// [offsets[e], offsets[e+1]) (or [0, K) when offsets is null), zeros past
+// the end; item = (e, m tile, n tile) from blockIdx; rows n >= n_split go to
+// out2; rows n >= n_valid are not stored.  M, n_total multiples of 128.
+struct BwdGemmArgs {
+  const uint16_t* a;
+  const uint16_t* a2;
+  int64_t lda;
+  int64_t a_gs;
+  int a_split;
+  int a_krows;
+  const uint16_t* b;
+  int64_t ldb;
+  const int32_t* b_gather;
+  int b_div;
+  const uint16_t* zeros;     // >= 128 zero bf16
+  int M, K;
+  int n_total, n_valid;
+  const Schedule* sched;
+  const int32_t* offsets;
+  void* out;
+  void* out2;
+  int64_t ldo;
+  int64_t o_gs;
+  int n_split;
+  int out_f32;
+};
+hipError_t launch_gemm_bwd(const BwdGemmArgs& a, int ragged_k, int grid, hipStream_t stream);
+hipError_t launch_swiglu_bwd(const float* ev, const float* gu, const int32_t* perm, const float* w, int64_t P,
+                             int I, int act, float* dw, uint16_t* ap, uint16_t* dgu, hipStream_t stream);
+hipError_t launch_router_bwd(const float* part, int slices, int64_t T, int E, int Epad, const float* bias,
+                             const int32_t* ids, const float* dw, int k, int score, int renorm, float routed_scale,
+                             float* dkey, uint16_t* dkey_b, hipStream_t stream);
+hipError_t launch_bias_grad(const float* dkey, int64_t T, int E, float* dbias, hipStream_t stream);
+hipError_t launch_dx_combine(const float* dxp, const float* dxr, const int32_t* inv, int64_t T, int k, int H,
+                             uint16_t* dx, hipStream_t stream);
+// bytes: multiple of 4
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t stream);
 
 // ---- combine
 hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const float* w, int64_t T,

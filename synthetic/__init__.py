@@ -246,5 +246,12 @@ def _fp4_experts(s: LayerSpec, seed: int, device) -> dict:
     return res
 
 
+def make_grad_out(s: LayerSpec, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Gradient of the layer output for the backward: N(0, 1) in the activation
+    dtype, [T, H]."""
+    g = _gen(device, seed, s.name, "dout", s.T)
+    return torch.randn(s.T, s.H, generator=g, device=device).to(_act_dtype(s))
+
+
 def to_device(layer: dict, device) -> dict:
     return {k: (None if v is None else v.to(device)) for k, v in layer.items()}

@@ -170,3 +170,21 @@ def test_stream_path_needs_packed_weights_and_small_batches():
     assert _status_of(_forward_nulls, moe.make_desc(64, 2048, 1408, 60, 4, path="stream")) == moe.MOE_EUNSUPPORTED
     d = moe.make_desc(64, 2048, 1408, 60, 4, path="stream", layout="packed")
     assert _status_of(_forward_nulls, d) == moe.MOE_EWORKSPACE   # valid request, no workspace given
+
+
+def test_backward_validation():
+    """moe_backward: bf16 row-major experts with H, I multiples of 128 only;
+    everything else is rejected on the host before any launch."""
+    ok = moe.make_desc(64, 256, 384, 16, 4, score="sigmoid", renormalize=True, routed_scale=2.5)
+    assert moe.moe_workspace_bytes(ok, moe.MOE_OP_BACKWARD) > 0
+    assert _status_of(lambda d: moe.moe_backward(d, *([None] * 13), stream=0), ok) == moe.MOE_EWORKSPACE
+    for d in (moe.make_desc(8, 7168, 2048, 256, 8, w_dtype="fp8", w_scale_fmt="f32"),
+              moe.make_desc(64, 256, 384, 16, 4, layout="packed"),
+              moe.make_desc(64, 192, 384, 16, 4),
+              moe.make_desc(64, 128, 128, 8, 2, act_dtype="f32", w_dtype="f32")):
+        assert moe.moe_workspace_bytes(d, moe.MOE_OP_BACKWARD) == 0
+        assert _status_of(lambda dd: moe.moe_backward(dd, *([None] * 13), stream=0), d) == moe.MOE_EUNSUPPORTED
+    empty = moe.make_desc(0, 256, 384, 16, 4)
+    assert moe.moe_workspace_bytes(empty, moe.MOE_OP_BACKWARD) == 0
+    # no token: the parameter gradients must be given (they are zero-filled)
+    assert _status_of(lambda d: moe.moe_backward(d, *([None] * 13), stream=0), empty) == moe.MOE_EINVAL
