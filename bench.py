@@ -1,7 +1,7 @@
 """Throughput of the routed mixture-of-experts layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T N]
-                    [--scale-fmt f32|ue8m0] [--no-cpu-baseline]
+                    [--scale-fmt f32|ue8m0] [--no-cpu-baseline] [--backward]
 
 A step is one moe_forward call (router, permutation, gate/up + SwiGLU, down,
 combine) over one batch of T synthetic tokens whose inputs and weights are
@@ -27,6 +27,10 @@ measurement.  The JSON line also carries:
   sample: the router over all T tokens plus the expert MLPs and the combine on
   a sample of tokens sized to about 10 s; tokens/s = 1 / (router time per
   token + expert time per token).
+
+--backward times moe_backward instead (every gradient of the layer, bf16
+row-major experts): value = T * K / elapsed, the roofline of its dominant GEMM
+stage, and the oracle's backward on a bounded sample as cpu_baseline.
 """
 from __future__ import annotations
 
@@ -67,6 +71,8 @@ def parse():
     p.add_argument("--graph", default="off", choices=["auto", "off"],
                    help="decode: replay each timed step as a captured HIP graph (auto) or launch eagerly "
                         "(off, the default: measured faster on this stack)")
+    p.add_argument("--backward", action="store_true",
+                   help="time moe_backward (every gradient of the layer) instead of the forward")
     p.add_argument("--flush", default="read", choices=["read", "write"],
                    help="decode: evict the last-level cache between timed steps by reading (default) "
                         "or by rewriting a 2 GiB buffer")
@@ -136,6 +142,130 @@ def cpu_baseline(s, L, budget_s: float):
                       % (s.T, t_route, done, t_exp)}
 
 
+def cpu_baseline_backward(s, L, dout, budget_s: float):
+    """Time the fp64 oracle's backward on a bounded sample of this workload."""
+    import numpy as np
+    import oracle
+
+    hl = {k: (None if v is None else v.detach().cpu()) for k, v in L.items()}
+    d64 = dout.detach().cpu().double().numpy()
+    score = oracle.SOFTMAX if s.score == "softmax" else oracle.SIGMOID
+    gate = {"silu": oracle.GATE_SILU, "gelu": oracle.GATE_GELU, "relu": oracle.GATE_RELU}[s.gate]
+    ex = oracle.Experts(hl["w_gate"], hl["w_up"], hl["w_down"], gate=gate)
+    t0 = time.perf_counter()
+    ids, w, keys = oracle.route(hl["x"], hl["w_router"], hl["router_bias"], s.k, score, s.renormalize,
+                                s.routed_scale, want_keys=True)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(s.T)
+    n, t_tok, done = 8, 0.0, 0
+    while done < s.T and t_tok < budget_s / 2:
+        batch = order[done:done + n]
+        t0 = time.perf_counter()
+        oracle.bwd_tokens(ex, hl["x"], hl["w_router"], score, s.renormalize, s.routed_scale, keys, ids, w, d64,
+                          batch)
+        t_tok += time.perf_counter() - t0
+        done += batch.size
+        n = int(min(max(8, (budget_s / 2 - t_tok) / (t_tok / done)), s.T - done))
+    # weight gradients: every row of the three matrices of the expert with the
+    # fewest (but at least 4) pairs, priced per pair
+    counts = np.bincount(ids.ravel(), minlength=s.E)
+    cand = np.nonzero(counts >= 4)[0]
+    e = int(cand[np.argmin(counts[cand])])
+    t0 = time.perf_counter()
+    for which, rows in ((oracle.BWD_GATE, s.I), (oracle.BWD_UP, s.I), (oracle.BWD_DOWN, s.H)):
+        oracle.bwd_expert_rows(ex, which, e, np.arange(rows), hl["x"], ids, w, d64)
+    t_w = time.perf_counter() - t0
+    per_token = t_route / s.T + t_tok / done + s.k * t_w / counts[e]
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "fp64 oracle backward: router on all %d tokens (%.2f s) + token gradients on %d sampled "
+                      "tokens (%.2f s) + all weight-gradient rows of expert %d over its %d pairs (%.2f s); "
+                      "tokens/s = 1/(router + token + k * weight-gradient-per-pair seconds)"
+                      % (s.T, t_route, done, t_tok, e, counts[e], t_w)}
+
+
+def bench_backward(args, s, L, dev):
+    """One step = one moe_backward over the batch; prints the JSON line."""
+    import torch
+    import mixture_experts_routed_softmax_amd as moe
+    import synthetic
+
+    if s.experts != "bf16":
+        print("the backward takes bf16 experts (workload %s has %s)" % (s.name, s.experts), file=sys.stderr)
+        sys.exit(2)
+    d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,
+                      routed_scale=s.routed_scale, gate=s.gate)
+    dout = synthetic.make_grad_out(s, seed=args.seed, device=dev)
+    dx = torch.empty_like(L["x"])
+    dwr = torch.empty_like(L["w_router"])
+    db = torch.empty(s.E, dtype=torch.float32, device=dev)
+    dwg, dwu, dwd = torch.empty_like(L["w_gate"]), torch.empty_like(L["w_up"]), torch.empty_like(L["w_down"])
+    ws = moe.workspace(d, moe.MOE_OP_BACKWARD, dev)
+
+    def step():
+        moe.moe_backward(d, L["x"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"], L["w_down"], dout,
+                         dx, dwr, db, dwg, dwu, dwd, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.moe_timing_enable(True)
+    moe.moe_timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed_ms = (time.perf_counter() - t0) * 1e3
+    stages = moe.moe_timing_read()
+    moe.moe_timing_enable(False)
+    ms_per_step = elapsed_ms / args.steps
+    value = s.T / (ms_per_step / 1e3)
+    for name, (ms, n) in stages.items():
+        if n:
+            log("  stage %-13s %8.1f us/step  (%d launches)" % (name, 1e3 * ms / args.steps, n))
+    P = s.T * s.k
+    # algorithmic FLOPs of the stages' GEMMs per step: data gradients e = W_down^T dout
+    # (2 P H I) and dx = [dg|du] [W_gate; W_up] (2 P 2I H); weight gradients
+    # dW_down (2 P H I) and dW_gate, dW_up (2 P 2I H); the recompute of g, u (2 P H 2I)
+    gemm = {"bwd_data": 6.0 * P * s.H * s.I, "bwd_weight": 6.0 * P * s.H * s.I,
+            "bwd_recompute": 4.0 * P * s.H * s.I}
+    dom = max(gemm, key=lambda k: stages[k][0])
+    ms_dom, n_dom = stages[dom]
+    per_launch_ms = ms_dom / n_dom
+    flops_per_launch = gemm[dom] * args.steps / n_dom
+    achieved = flops_per_launch / (per_launch_ms / 1e3) / 1e12
+    total_flops = 16.0 * P * s.H * s.I
+    log("backward: %.3f ms/step, %.0f tokens/s, %.1f TFLOP/s over the expert GEMMs (recompute included)"
+        % (ms_per_step, value, total_flops / (ms_per_step / 1e3) / 1e12))
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None,
+            "kernel": {"bwd_data": "gemm_bwd_kernel<0> (data-gradient GEMMs)",
+                       "bwd_weight": "gemm_bwd_kernel<1> (weight-gradient GEMMs)",
+                       "bwd_recompute": "gemm_bf16_kernel<0, false> (recompute of g, u)"}[dom],
+            "avg_launch_us": round(per_launch_ms * 1e3, 2), "alg_flops_per_launch": flops_per_launch}
+    cpu = None
+    if not args.no_cpu_baseline:
+        del ws, dwg, dwu, dwd
+        cpu = cpu_baseline_backward(s, L, dout, args.cpu_seconds)
+        log("cpu baseline: %.2f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+    line = {
+        "metric": "MoE-layer backward tokens/s (every gradient of the layer); % MFMA peak of the dominant "
+                  "backward GEMM",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name + "_backward", "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
+                   "experts": s.experts, "score": s.score, "renormalize": s.renormalize,
+                   "routed_scale": s.routed_scale, "router_bias": s.bias, "weights": "rowmajor",
+                   **({"gate": s.gate} if s.gate != "silu" else {}),
+                   "gemm_tflops": round(total_flops / (ms_per_step / 1e3) / 1e12, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -171,6 +301,9 @@ def main():
     L = synthetic.make_layer(s, seed=args.seed, device=dev)
     torch.cuda.synchronize()
     log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+    if args.backward:
+        bench_backward(args, s, L, dev)
+        return
 
     layout = args.layout if s.experts != "f32" else "rowmajor"
     d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,

@@ -466,6 +466,22 @@ moe_desc backward_desc(const moe_desc* d) {
 
 int expert_pad(int E) { return (E + 127) / 128 * 128; }
 
+// dW_r = dkey^T x reduces over all T tokens: the K range is split into chunks
+// of k_chunk rows (a multiple of 32) so that about 512 workgroups run; the
+// fp32 partial sums are added in chunk order afterwards
+int router_chunks(const moe_desc* d, int* k_chunk) {
+  const int64_t per_chunk = (int64_t)(d->H / 128) * (expert_pad(d->E) / 128);
+  int64_t chunks = (512 + per_chunk - 1) / per_chunk;
+  const int64_t max_chunks = (d->T + 255) / 256;
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  int64_t kc = (d->T + chunks - 1) / chunks;
+  kc = (kc + 31) / 32 * 32;
+  chunks = (d->T + kc - 1) / kc;
+  *k_chunk = (int)kc;
+  return (int)chunks;
+}
+
 struct BackwardWs {
   float* route_part;
   int32_t* ids;
@@ -490,6 +506,7 @@ struct BackwardWs {
   float* dkey;
   uint16_t* dkey_b;
   float* dxr;
+  float* dwr_part;
   uint16_t* zeros;
 };
 
@@ -522,6 +539,8 @@ BackwardWs carve_backward(Carve& c, const moe_desc* d0) {
   w.dkey = c.take<float>((size_t)d->T * d->E);
   w.dkey_b = c.take<uint16_t>((size_t)d->T * expert_pad(d->E));
   w.dxr = c.take<float>((size_t)d->T * H);
+  int kc = 0;
+  w.dwr_part = c.take<float>((size_t)router_chunks(d, &kc) * d->E * H);
   w.zeros = c.take<uint16_t>(128);
   return w;
 }
@@ -884,6 +903,8 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
                                   d->k, d->score, d->renormalize, d->routed_scale, bw.dkey, bw.dkey_b, st),
                 "router backward launch");
     if (d_bias) MOE_TRY_HIP(launch_bias_grad(bw.dkey, d->T, E, d_bias, st), "bias gradient launch");
+    int kc = 0;
+    const int chunks = router_chunks(d, &kc);
     BwdGemmArgs g{};
     g.a = (const uint16_t*)x;
     g.lda = H;
@@ -892,11 +913,15 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.zeros = bw.zeros;
     g.M = H;
     g.K = (int)d->T;
+    g.k_chunk = kc;
     g.n_total = Epad;
     g.n_valid = E;
-    g.out = dw_router;
+    g.out = bw.dwr_part;
     g.ldo = H;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, (H / 128) * (Epad / 128), st), "backward GEMM launch");
+    g.o_gs = (int64_t)E * H;
+    g.out_f32 = 1;
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, chunks * (H / 128) * (Epad / 128), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_chunk_sum(bw.dwr_part, chunks, (int64_t)E * H, (uint16_t*)dw_router, st), "sum launch");
     g = BwdGemmArgs{};
     g.a = (const uint16_t*)w_router;
     g.lda = H;

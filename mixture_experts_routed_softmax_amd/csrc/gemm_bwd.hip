@@ -23,7 +23,8 @@
 // v_mfma_f32_32x32x16_bf16 needs.
 //
 // Tile 128 (M) x 128 (N), K step 32, 4 waves of 64 x 64 (2 x 2 MFMA tiles),
-// 4 LDS stages of 16 KB (two workgroups per CU).  MN-major stages hold 32 K
+// 4 LDS stages of 16 KB (two workgroups per CU); the fragments of step s+1
+// are read from LDS while the MFMAs of step s run.  MN-major stages hold 32 K
 // rows of 256 B with 16-byte chunk c of row r at c ^ 4 (r & 3): the 16 lanes
 // of a transposed read touch 16 distinct chunks (all 64 banks).  K-major
 // stages hold 128 rows of 64 B with chunk c at c ^ ((r >> 2) & 3).
@@ -61,6 +62,10 @@ __device__ __forceinline__ int mn_off(int r, int col) {
 // byte offset of 16-byte chunk c of row r in a K-major stage
 __device__ __forceinline__ int km_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ v4s tr_read(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
 }
@@ -96,6 +101,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void gemm_bwd_kernel(BwdGemmArgs a)
     if (a.offsets) {
       kbase = a.offsets[e];
       nK = a.offsets[e + 1] - a.offsets[e];
+    } else if (a.k_chunk > 0) {   // group e = K rows [e k_chunk, (e+1) k_chunk) of K
+      kbase = (int64_t)e * a.k_chunk;
+      nK = a.K - (int)kbase < a.k_chunk ? a.K - (int)kbase : a.k_chunk;
     } else {
       nK = a.K;
     }
@@ -177,19 +185,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void gemm_bwd_kernel(BwdGemmArgs a)
   const int nvalid = kRK ? 128 : re - rb;
   const bool live0 = wn * 64 < nvalid, live1 = wn * 64 + 32 < nvalid;
 
-#pragma unroll
-  for (int p = 0; p < kStagesB - 1; ++p)
-    if (p < KT) issue(p, p);
-  for (int s = 0; s < KT; ++s) {
-    const int ahead = KT - 1 - s;   // steps issued after step s
-    if (ahead >= 2) wait_vm<2 * kLoadsB>();
-    else if (ahead == 1) wait_vm<kLoadsB>();
-    else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + kStagesB - 1 < KT) issue((s + kStagesB - 1) % kStagesB, s + kStagesB - 1);
-    const uint8_t* st = smem + (s % kStagesB) * kStageB;
-    bf16x8 fa[2][2], fb[2][2];
+  // fragments of one K step: [h][tile] for A and B
+  typedef bf16x8 Frags[2][2];
+  auto read_frags = [&](int stage, Frags& fa, Frags& fb) {
+    const uint8_t* st = smem + stage * kStageB;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -200,14 +199,47 @@ __global__ __launch_bounds__(kBwdThreads, 2) void gemm_bwd_kernel(BwdGemmArgs a)
         else fb[h][t] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 64 + t * 32 + l32, h * 2 + hl));
       }
     }
+  };
+  auto mfmas = [&](const Frags& fa, const Frags& fb) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
-        if (live0) acc[ti][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][ti], fb[h][0], acc[ti][0], 0, 0, 0);
-        if (live1) acc[ti][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][ti], fb[h][1], acc[ti][1], 0, 0, 0);
+        if (live0) acc[ti][0] = mfma_bf16(fa[h][ti], fb[h][0], acc[ti][0]);
+        if (live1) acc[ti][1] = mfma_bf16(fa[h][ti], fb[h][1], acc[ti][1]);
       }
+  };
+  // One K step: once step s+1 has landed (and every wave is past step s-1's
+  // stage), refill that stage with step s+3, read step s+1's fragments and run
+  // step s's MFMAs from the fragments read one step earlier.
+  auto body = [&](int s, const Frags& ca, const Frags& cb, Frags& na, Frags& nb) {
+    if (s + 1 < KT) {
+      if (KT - 2 - s >= 1) wait_vm<kLoadsB>();
+      else wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + kStagesB - 1 < KT) issue((s + kStagesB - 1) % kStagesB, s + kStagesB - 1);
+      read_frags((s + 1) % kStagesB, na, nb);
+    }
+    mfmas(ca, cb);
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Frags fa0, fb0, fa1, fb1;
+  if (KT > 0) {
+#pragma unroll
+    for (int p = 0; p < kStagesB - 1; ++p)
+      if (p < KT) issue(p, p);
+    if (KT >= 3) wait_vm<2 * kLoadsB>();
+    else if (KT == 2) wait_vm<kLoadsB>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, fa0, fb0);
+  }
+  for (int s = 0; s < KT; s += 2) {
+    body(s, fa0, fb0, fa1, fb1);
+    if (s + 1 < KT) body(s + 1, fa1, fb1, fa0, fb0);
   }
 
   // ---- epilogue: lane holds C[m][n] for n = l32 of each B tile and
@@ -407,6 +439,20 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
   *(i32x2*)(dx + t * H + c) = i32x2{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3])};
 }
 
+// out[i] = bf16(sum_c part[c][i]) over the K chunks in order
+__global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict__ part, int chunks, int64_t n,
+                                                       uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *(const f32x4*)(part + i);
+  for (int c = 1; c < chunks; ++c) {
+    const f32x4 v = *(const f32x4*)(part + (int64_t)c * n + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += v[q];
+  }
+  *(i32x2*)(out + i) = i32x2{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3])};
+}
+
 __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0u;
@@ -447,6 +493,13 @@ hipError_t launch_dx_combine(const float* dxp, const float* dxr, const int32_t* 
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(dx_combine_kernel, dim3((unsigned)T, (unsigned)((H / 4 + 255) / 256)), dim3(256), 0, stream, dxp,
                      dxr, inv, k, H, dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_sum(const float* part, int chunks, int64_t n, uint16_t* out, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, part, chunks, n,
+                     out);
   return hipGetLastError();
 }
 

@@ -137,6 +137,8 @@ hipError_t launch_down_f32(const GemmArgs& a, hipStream_t stream);
 // [offsets[e], offsets[e+1]) (or [0, K) when offsets is null), zeros past
 // the end; item = (e, m tile, n tile) from blockIdx; rows n >= n_split go to
 // out2; rows n >= n_valid are not stored.  M, n_total multiples of 128.
+// Without offsets, k_chunk > 0 splits K: group e takes K rows
+// [e k_chunk, (e+1) k_chunk) (partial sums, one output slice per group).
 struct BwdGemmArgs {
   const uint16_t* a;
   const uint16_t* a2;
@@ -159,6 +161,7 @@ struct BwdGemmArgs {
   int64_t o_gs;
   int n_split;
   int out_f32;
+  int k_chunk;
 };
 hipError_t launch_gemm_bwd(const BwdGemmArgs& a, int ragged_k, int grid, hipStream_t stream);
 hipError_t launch_swiglu_bwd(const float* ev, const float* gu, const int32_t* perm, const float* w, int64_t P,
@@ -171,6 +174,8 @@ hipError_t launch_dx_combine(const float* dxp, const float* dxr, const int32_t* 
                              uint16_t* dx, hipStream_t stream);
 // bytes: multiple of 4
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t stream);
+// out[i] = bf16(sum over c < chunks of part[c * n + i]), n a multiple of 4
+hipError_t launch_chunk_sum(const float* part, int chunks, int64_t n, uint16_t* out, hipStream_t stream);
 
 // ---- combine
 hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const float* w, int64_t T,
