@@ -179,6 +179,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     ch = ch < N ? ch : N - 1;   // rows past N are zero in the packed tile
     ssrc = sm + ((int64_t)e * N + ch) * (K / 32);
   }
+  // token DMA instructions that carry live rows: the second one (rows
+  // kTok/2 .. kTok-1) is skipped when the tile holds no row there; its LDS
+  // rows are then read by no wave (their waves have no live token tile)
+  const int live_bi = __builtin_amdgcn_readfirstlane(kBI == 2 && valid <= kTok / 2 ? 1 : kBI);
+  const bool full_loads = live_bi == kBI;
   // wave-uniform parts of the DMA addresses (M0 takes the LDS address)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint8_t* asrc = abase + lane * 16 + wv * 1024;
@@ -188,7 +193,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     lds_load16(src, sb);
     lds_load16(src + 8192, sb + 8192);
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) lds_load16(bsrc[i] + (int64_t)kt * kTokRowB, sb + kA + i * 8192);
+    for (int i = 0; i < kBI; ++i)
+      if (i < live_bi) lds_load16(bsrc[i] + (int64_t)kt * kTokRowB, sb + kA + i * 8192);
     if constexpr (kFp4)
       __builtin_amdgcn_global_load_lds(ssrc + kt * 4, (lds_ptr)(smem + stage * kStage + kA + kB + (wv & 3) * 256), 4,
                                        0, 0);
@@ -357,6 +363,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     }
   };
 
+  // s_waitcnt until at most `ahead` K steps of this thread's DMA are in flight
+  auto wait_ahead = [&](int ahead) {
+    if (full_loads) wait_steps<kLoads>(ahead);
+    else wait_steps<kLoads - 1>(ahead);
+  };
   auto mainloop = [&](auto nt_const) {
     constexpr int NT = decltype(nt_const)::value;
     constexpr std::integral_constant<int, 0> h0{};
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < kStages - 1; ++p)
       if (p < KT) issue(p, p);
-    wait_steps<kLoads>((KT < kStages - 1 ? KT : kStages - 1) - 1);
+    wait_ahead((KT < kStages - 1 ? KT : kStages - 1) - 1);
     __builtin_amdgcn_s_barrier();   // bare barrier: __syncthreads would wait for every step in flight
     F f;
     read_half(0, f, h0, nt_const);
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     // number of steps still in flight behind step s+1 is constant
     for (; s < KT - (kStages - 1); ++s) {
       const int next = stage + 1 == kStages ? 0 : stage + 1;
-      wait_vmcnt<(kStages - 3) * kLoads>();   // step s+1 landed for this thread
+      wait_ahead(kStages - 3);                // step s+1 landed for this thread
       __builtin_amdgcn_s_barrier();           // ... and for all; step s-1's stage is free
       issue(fill, s + kStages - 1);
       fill = fill + 1 == kStages ? 0 : fill + 1;
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     // drain: nothing left to issue
     for (; s + 1 < KT; ++s) {
       const int next = stage + 1 == kStages ? 0 : stage + 1;
-      wait_steps<kLoads>(KT - 2 - s);
+      wait_ahead(KT - 2 - s);
       __builtin_amdgcn_s_barrier();
       body(s, next);
       stage = next;
