@@ -466,11 +466,21 @@ moe_desc backward_desc(const moe_desc* d) {
 
 int expert_pad(int E) { return (E + 127) / 128 * 128; }
 
+// tiles of the backward GEMM along an extent n (kBwdTile rows or columns each)
+int bwd_tiles(int64_t n) { return (int)((n + kBwdTile - 1) / kBwdTile); }
+
+// ragged-row schedule of a backward GEMM: kBwdTile token rows per tile
+SchedRequest bwd_sched_req(Schedule* s, const moe_desc* d, int ntiles) {
+  SchedRequest r = sched_req(s, d, ntiles);
+  r.rows_per_tile = kBwdTile;
+  return r;
+}
+
 // dW_r = dkey^T x reduces over all T tokens: the K range is split into chunks
 // of k_chunk rows (a multiple of 32) so that about 512 workgroups run; the
 // fp32 partial sums are added in chunk order afterwards
 int router_chunks(const moe_desc* d, int* k_chunk) {
-  const int64_t per_chunk = (int64_t)(d->H / 128) * (expert_pad(d->E) / 128);
+  const int64_t per_chunk = (int64_t)bwd_tiles(d->H) * bwd_tiles(expert_pad(d->E));
   int64_t chunks = (512 + per_chunk - 1) / per_chunk;
   const int64_t max_chunks = (d->T + 255) / 256;
   if (chunks > max_chunks) chunks = max_chunks;
@@ -526,8 +536,8 @@ BackwardWs carve_backward(Carve& c, const moe_desc* d0) {
   w.inv = c.take<int32_t>(P);
   w.touched = c.take<int32_t>(d->E + 1);
   w.sched_gu = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, gate_up_ntiles(d))));
-  w.sched_e = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, d->I / 128)));
-  w.sched_dx = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, d->H / 128)));
+  w.sched_e = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, bwd_tiles(d->I))));
+  w.sched_dx = (Schedule*)c.take<uint8_t>(sched_bytes(sched_capacity(d, bwd_tiles(d->H))));
   w.x_sorted = c.take<uint16_t>((size_t)P * H);
   w.dout_sorted = c.take<uint16_t>((size_t)P * H);
   w.gu = c.take<float>((size_t)P * 2 * I);
@@ -793,8 +803,8 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
                 "router launch");
   }
   const SchedRequest sgu = sched_req(bw.sched_gu, d, gate_up_ntiles(d));
-  const SchedRequest se = sched_req(bw.sched_e, d, I / 128);
-  const SchedRequest sdx = sched_req(bw.sched_dx, d, H / 128);
+  const SchedRequest se = bwd_sched_req(bw.sched_e, d, bwd_tiles(I));
+  const SchedRequest sdx = bwd_sched_req(bw.sched_dx, d, bwd_tiles(H));
   if ((s = run_permute(d, bw.ids, bw.counts, bw.offsets, bw.perm, bw.inv, bw.touched, bw.pw, sgu, se, st)) != MOE_OK)
     return s;
   {
@@ -878,7 +888,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.out = dw_down;
     g.ldo = I;
     g.o_gs = (int64_t)H * I;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * (I / 128) * (H / 128), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * bwd_tiles(I) * bwd_tiles(H), st), "backward GEMM launch");
     // dW_gate[e], dW_up[e] = sum over the expert's rows of [dg | du] x^T
     g = BwdGemmArgs{};
     g.a = bw.x_sorted;
@@ -894,7 +904,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.n_split = I;
     g.ldo = H;
     g.o_gs = (int64_t)I * H;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * (H / 128) * (2 * I / 128), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * bwd_tiles(H) * bwd_tiles(2 * I), st), "backward GEMM launch");
   }
   {
     // router: key gradients, dW_r = dkey^T x, dbias, and dkey . W_r into dx
@@ -920,7 +930,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.ldo = H;
     g.o_gs = (int64_t)E * H;
     g.out_f32 = 1;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, chunks * (H / 128) * (Epad / 128), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, chunks * bwd_tiles(H) * bwd_tiles(Epad), st), "backward GEMM launch");
     MOE_TRY_HIP(launch_chunk_sum(bw.dwr_part, chunks, (int64_t)E * H, (uint16_t*)dw_router, st), "sum launch");
     g = BwdGemmArgs{};
     g.a = (const uint16_t*)w_router;
@@ -935,7 +945,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.out = bw.dxr;
     g.ldo = H;
     g.out_f32 = 1;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 0, (int)((d->T + 127) / 128) * (H / 128), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, bwd_tiles(d->T) * bwd_tiles(H), st), "backward GEMM launch");
   }
   {
     StageTimer tm(MOE_STAGE_BWD_MISC, st);

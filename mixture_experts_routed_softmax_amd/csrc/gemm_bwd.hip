@@ -22,12 +22,13 @@
 // transposed 4 x 16 block.  Two such reads form the 8 K values a lane of
 // v_mfma_f32_32x32x16_bf16 needs.
 //
-// Tile 128 (M) x 128 (N), K step 32, 4 waves of 64 x 64 (2 x 2 MFMA tiles),
-// 4 LDS stages of 16 KB (two workgroups per CU); the fragments of step s+1
-// are read from LDS while the MFMAs of step s run.  MN-major stages hold 32 K
-// rows of 256 B with 16-byte chunk c of row r at c ^ 4 (r & 3): the 16 lanes
+// Tile 256 (M) x 256 (N), K step 32, 8 waves of 64 x 128 (2 x 4 MFMA tiles),
+// 4 LDS stages of 32 KB (one workgroup per CU).  MN-major stages hold 32 K
+// rows of 512 B with 16-byte chunk c of row r at c ^ 4 (r & 3): the 16 lanes
 // of a transposed read touch 16 distinct chunks (all 64 banks).  K-major
-// stages hold 128 rows of 64 B with chunk c at c ^ ((r >> 2) & 3).
+// stages hold 256 rows of 64 B with chunk c at c ^ ((r >> 2) & 3).  Columns
+// past M or N read zeros and are not stored; MFMA tiles without live rows or
+// columns are skipped.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,8 +36,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kBwdThreads = 256;
-constexpr int kOpBytes = 8192;                 // one operand per stage
+constexpr int kBwdThreads = 512;
+constexpr int kTile = kBwdTile;                // M and N extent of a tile
+constexpr int kOpBytes = kTile * 64;           // one operand per stage: 32 K x 256 bf16
 constexpr int kStageB = 2 * kOpBytes;
 constexpr int kStagesB = 4;
 constexpr int kLoadsB = 4;                     // DMA instructions per thread per stage
@@ -55,11 +57,11 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// byte offset of element `col` of K row r in an MN-major stage
+// byte offset of element `col` of K row r in an MN-major stage (512-byte rows)
 __device__ __forceinline__ int mn_off(int r, int col) {
-  return r * 256 + ((((col >> 3) ^ ((r & 3) << 2))) << 4) + (col & 7) * 2;
+  return r * 512 + ((((col >> 3) ^ ((r & 3) << 2))) << 4) + (col & 7) * 2;
 }
-// byte offset of 16-byte chunk c of row r in a K-major stage
+// byte offset of 16-byte chunk c of row r in a K-major stage (64-byte rows)
 __device__ __forceinline__ int km_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -81,18 +83,19 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint8_t* st, int h, int m0, int 
 }
 
 template <int kRK>
-__global__ __launch_bounds__(kBwdThreads, 2) void gemm_bwd_kernel(BwdGemmArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStagesB * kStageB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;     // wave tile: M 64 (2 MFMA tiles) x N 128 (4 tiles)
 
   // ---- work item
   int e, mt, nt = 0, rb = 0, re = 0;
   int64_t kbase = 0;
   int nK;
+  const int MT = (a.M + kTile - 1) / kTile;
   if (kRK) {
-    const int MT = a.M / 128, NT = a.n_total / 128;
+    const int NT = (a.n_total + kTile - 1) / kTile;
     const int item = blockIdx.x;
     e = item / (MT * NT);
     const int rem = item - e * MT * NT;
@@ -117,30 +120,37 @@ __global__ __launch_bounds__(kBwdThreads, 2) void gemm_bwd_kernel(BwdGemmArgs a)
       rb = it.row_begin;
       re = it.row_end;
     } else {
-      const int MT = a.M / 128;
       const int tile = blockIdx.x / MT;
       mt = blockIdx.x - tile * MT;
       e = 0;
-      rb = tile * 128;
+      rb = tile * kTile;
       if (rb >= a.n_total) return;
-      re = rb + 128 < a.n_total ? rb + 128 : a.n_total;
+      re = rb + kTile < a.n_total ? rb + kTile : a.n_total;
     }
     nK = a.K;
   }
   const int KT = (nK + 31) / 32;
 
   // ---- loaders.  MN-major operand: instruction i of wave w fills K rows
-  // (i*4 + w)*4 .. +4 of the stage, lane -> row lane/16, chunk slot lane%16.
-  const int mn_r = lane >> 4;                       // row within the wave's 4 rows (== row & 3)
-  const int mn_c = (lane & 15) ^ (mn_r << 2);       // global chunk this lane fetches
-  const int m0 = mt * 128 + mn_c * 8;
-  const int n0 = nt * 128 + mn_c * 8;
-  // K-major B (ragged N): instruction i of wave w fills rows (i*4 + w)*16 .. +16
+  // (i*8 + w)*2 .. +2 of the stage; lane -> row lane/32, chunk slot lane%32
+  // holding global chunk slot ^ 4 (row & 3).  Chunks past the operand's
+  // extent (M, or n_total) read zeros.
+  const int mn_r = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int mcol[2], ncol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = (i * 8 + wave) * 2 + mn_r;
+    const int c = (lane & 31) ^ ((rr & 3) << 2);
+    mcol[i] = mt * kTile + c * 8;
+    ncol[i] = nt * kTile + c * 8;
+  }
+  // K-major B (ragged N): instruction i of wave w fills rows (i*8 + w)*16 .. +16
   const uint16_t* brow[2] = {nullptr, nullptr};
   if (!kRK) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int rr = (i * 4 + wave) * 16 + (lane >> 2);
+      const int rr = (i * 8 + wave) * 16 + (lane >> 2);
       int r = rb + rr;
       r = r < re ? r : re - 1;
       const int64_t src = a.b_gather ? (int64_t)(a.b_gather[r] / a.b_div) : (int64_t)r;
@@ -148,124 +158,103 @@ __global__ __launch_bounds__(kBwdThreads, 2) void gemm_bwd_kernel(BwdGemmArgs a)
       brow[i] = a.b + src * a.ldb + c * 8;
     }
   }
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto a_src = [&](int kr) -> const uint16_t* {   // K row kr (0-based within the item) of A
-    if (kr >= nK) return a.zeros + mn_c * 8;
-    if (kRK) return a.a + (kbase + kr) * a.lda + m0;
-    if (kr >= a.a_krows) return a.zeros + mn_c * 8;
-    if (kr < a.a_split) return a.a + (int64_t)e * a.a_gs + (int64_t)kr * a.lda + m0;
-    return a.a2 + (int64_t)e * a.a_gs + (int64_t)(kr - a.a_split) * a.lda + m0;
+  auto a_src = [&](int kr, int i) -> const uint16_t* {   // K row kr (item-relative) of A, this lane's chunk
+    if (kr >= nK || mcol[i] >= a.M) return a.zeros;
+    if (kRK) return a.a + (kbase + kr) * a.lda + mcol[i];
+    if (kr >= a.a_krows) return a.zeros;
+    if (kr < a.a_split) return a.a + (int64_t)e * a.a_gs + (int64_t)kr * a.lda + mcol[i];
+    return a.a2 + (int64_t)e * a.a_gs + (int64_t)(kr - a.a_split) * a.lda + mcol[i];
   };
   auto issue = [&](int stage, int kt) {
     uint8_t* st = smem + stage * kStageB;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int kr = kt * 32 + (i * 4 + wv) * 4 + mn_r;
-      dma16(a_src(kr), st + (i * 4 + wv) * 1024);
+      const int kr = kt * 32 + (i * 8 + wv) * 2 + mn_r;
+      dma16(a_src(kr, i), st + (i * 8 + wv) * 1024);
     }
     if (kRK) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int kr = kt * 32 + (i * 4 + wv) * 4 + mn_r;
-        const uint16_t* src = kr < nK ? a.b + (kbase + kr) * a.ldb + n0 : a.zeros + mn_c * 8;
-        dma16(src, st + kOpBytes + (i * 4 + wv) * 1024);
+        const int kr = kt * 32 + (i * 8 + wv) * 2 + mn_r;
+        const uint16_t* src = kr < nK && ncol[i] < a.n_total ? a.b + (kbase + kr) * a.ldb + ncol[i] : a.zeros;
+        dma16(src, st + kOpBytes + (i * 8 + wv) * 1024);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(brow[i] + kt * 32, st + kOpBytes + (i * 4 + wv) * 1024);
+      for (int i = 0; i < 2; ++i) dma16(brow[i] + kt * 32, st + kOpBytes + (i * 8 + wv) * 1024);
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  // B tiles of this wave that hold live rows (ragged N)
-  const int nvalid = kRK ? 128 : re - rb;
-  const bool live0 = wn * 64 < nvalid, live1 = wn * 64 + 32 < nvalid;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // live MFMA tiles of this wave: M columns inside M, N rows inside the item
+  const int nvalid = kRK ? a.n_total - nt * kTile : re - rb;
+  int my_nt = (nvalid - wn * 128 + 31) / 32;
+  my_nt = my_nt < 0 ? 0 : (my_nt > 4 ? 4 : my_nt);
+  int my_mt = (a.M - mt * kTile - wm * 64 + 31) / 32;
+  my_mt = my_mt < 0 ? 0 : (my_mt > 2 ? 2 : my_mt);
 
-  // fragments of one K step: [h][tile] for A and B
-  typedef bf16x8 Frags[2][2];
-  auto read_frags = [&](int stage, Frags& fa, Frags& fb) {
-    const uint8_t* st = smem + stage * kStageB;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) fa[h][t] = frag_mn(st, h, wm * 64 + t * 32, lane);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (kRK) fb[h][t] = frag_mn(st + kOpBytes, h, wn * 64 + t * 32, lane);
-        else fb[h][t] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 64 + t * 32 + l32, h * 2 + hl));
-      }
-    }
-  };
-  auto mfmas = [&](const Frags& fa, const Frags& fb) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-        if (live0) acc[ti][0] = mfma_bf16(fa[h][ti], fb[h][0], acc[ti][0]);
-        if (live1) acc[ti][1] = mfma_bf16(fa[h][ti], fb[h][1], acc[ti][1]);
-      }
-  };
-  // One K step: once step s+1 has landed (and every wave is past step s-1's
-  // stage), refill that stage with step s+3, read step s+1's fragments and run
-  // step s's MFMAs from the fragments read one step earlier.
-  auto body = [&](int s, const Frags& ca, const Frags& cb, Frags& na, Frags& nb) {
-    if (s + 1 < KT) {
-      if (KT - 2 - s >= 1) wait_vm<kLoadsB>();
-      else wait_vm<0>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + kStagesB - 1 < KT) issue((s + kStagesB - 1) % kStagesB, s + kStagesB - 1);
-      read_frags((s + 1) % kStagesB, na, nb);
-    }
-    mfmas(ca, cb);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  Frags fa0, fb0, fa1, fb1;
-  if (KT > 0) {
-#pragma unroll
-    for (int p = 0; p < kStagesB - 1; ++p)
-      if (p < KT) issue(p, p);
-    if (KT >= 3) wait_vm<2 * kLoadsB>();
-    else if (KT == 2) wait_vm<kLoadsB>();
+  for (int p = 0; p < kStagesB - 1; ++p)
+    if (p < KT) issue(p, p);
+  for (int s = 0; s < KT; ++s) {
+    const int ahead = KT - 1 - s;   // steps issued after step s
+    if (ahead >= 2) wait_vm<2 * kLoadsB>();
+    else if (ahead == 1) wait_vm<kLoadsB>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, fa0, fb0);
-  }
-  for (int s = 0; s < KT; s += 2) {
-    body(s, fa0, fb0, fa1, fb1);
-    if (s + 1 < KT) body(s + 1, fa1, fb1, fa0, fb0);
+    if (s + kStagesB - 1 < KT) issue((s + kStagesB - 1) % kStagesB, s + kStagesB - 1);
+    const uint8_t* st = smem + (s % kStagesB) * kStageB;
+    if (my_mt > 0 && my_nt > 0) {
+      bf16x8 fa[2][2], fb[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) fa[h][t] = frag_mn(st, h, wm * 64 + t * 32, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (kRK) fb[h][j] = frag_mn(st + kOpBytes, h, wn * 128 + j * 32, lane);
+          else fb[h][j] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 128 + j * 32 + l32, h * 2 + hl));
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            if (j < my_nt && t < my_mt) acc[t][j] = mfma_bf16(fa[h][t], fb[h][j], acc[t][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: lane holds C[m][n] for n = l32 of each B tile and
   // m = (r/4)*8 + hl*4 + r%4 of each A tile; out[n][m], 4 consecutive m per store
 #pragma unroll
-  for (int tj = 0; tj < 2; ++tj) {
-    int n;
+  for (int tj = 0; tj < 4; ++tj) {
+    const int rr = wn * 128 + tj * 32 + l32;
     uint8_t* orow;
     if (kRK) {
-      n = nt * 128 + wn * 64 + tj * 32 + l32;
+      const int n = nt * kTile + rr;
       if (n >= a.n_valid) continue;
       const bool second = a.out2 && n >= a.n_split;
       const int nn = second ? n - a.n_split : n;
       uint8_t* base = (uint8_t*)(second ? a.out2 : a.out);
       orow = base + ((int64_t)e * a.o_gs + (int64_t)nn * a.ldo) * (a.out_f32 ? 4 : 2);
     } else {
-      const int rr = wn * 64 + tj * 32 + l32;
       if (rr >= nvalid) continue;
-      n = rb + rr;
-      orow = (uint8_t*)a.out + (int64_t)n * a.ldo * (a.out_f32 ? 4 : 2);
+      orow = (uint8_t*)a.out + (int64_t)(rb + rr) * a.ldo * (a.out_f32 ? 4 : 2);
     }
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = mt * 128 + wm * 64 + ti * 32 + q * 8 + hl * 4;
+        const int m = mt * kTile + wm * 64 + ti * 32 + q * 8 + hl * 4;
+        if (m >= a.M) continue;
         const f32x16& c = acc[ti][tj];
         if (a.out_f32) {
           *(f32x4*)(orow + (int64_t)m * 4) = f32x4{c[q * 4 + 0], c[q * 4 + 1], c[q * 4 + 2], c[q * 4 + 3]};

@@ -136,9 +136,11 @@ hipError_t launch_down_f32(const GemmArgs& a, hipStream_t stream);
 // zeros past a_krows; K = a.K.  ragged K: A and B MN-major, K rows
 // [offsets[e], offsets[e+1]) (or [0, K) when offsets is null), zeros past
 // the end; item = (e, m tile, n tile) from blockIdx; rows n >= n_split go to
-// out2; rows n >= n_valid are not stored.  M, n_total multiples of 128.
+// out2; rows n >= n_valid are not stored.  Tiles are kBwdTile x kBwdTile;
+// columns past M (A) or n_total (B) read zeros and are not stored.
 // Without offsets, k_chunk > 0 splits K: group e takes K rows
 // [e k_chunk, (e+1) k_chunk) (partial sums, one output slice per group).
+constexpr int kBwdTile = 256;
 struct BwdGemmArgs {
   const uint16_t* a;
   const uint16_t* a2;
@@ -150,7 +152,7 @@ struct BwdGemmArgs {
   int64_t ldb;
   const int32_t* b_gather;
   int b_div;
-  const uint16_t* zeros;     // >= 128 zero bf16
+  const uint16_t* zeros;     // >= 8 zero bf16
   int M, K;
   int n_total, n_valid;
   const Schedule* sched;
