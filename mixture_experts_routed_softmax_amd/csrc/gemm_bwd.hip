@@ -68,17 +68,18 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, co
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ v4s tr_read(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
-}
-
-// MFMA fragment of columns m0 .. m0+31, K half h (16 rows) of an MN-major stage
+// MFMA fragment of columns m0 .. m0+31, K half h (16 rows) of an MN-major stage.
+// The two transposed reads (K rows r and r+4: 2048 bytes apart, same swizzle)
+// are issued by inline assembly: the compiler treats the ds_read_tr builtin as
+// possibly aliasing the LDS DMA in flight and would wait for all of it before
+// each read.  The caller waits (lgkmcnt) before any use of the result.
 __device__ __forceinline__ bf16x8 frag_mn(const uint8_t* st, int h, int m0, int lane) {
   const int G = lane >> 4, s = lane & 15;
   const int col = m0 + (G & 1) * 16 + 4 * (s & 3);
   const int r = h * 16 + (G >> 1) * 8 + (s >> 2);
-  const v4s lo = tr_read(st + mn_off(r, col));
-  const v4s hi = tr_read(st + mn_off(r + 4, col));
+  const uint32_t a0 = (uint32_t)(uintptr_t)(lds_void)(st + mn_off(r, col));
+  v4s lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048" : "=&v"(lo), "=&v"(hi) : "v"(a0));
   return __builtin_bit_cast(bf16x8, v8s{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
 }
 
@@ -221,6 +222,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a)
           else fb[h][j] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 128 + j * 32 + l32, h * 2 + hl));
         }
       }
+      // the transposed reads land before any MFMA reads a fragment: the wait
+      // names every fragment as an operand, so no use can move above it
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fb[0][0]),
+                     "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3]), "+v"(fb[1][0]), "+v"(fb[1][1]),
+                     "+v"(fb[1][2]), "+v"(fb[1][3]));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
