@@ -211,9 +211,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a)
     if (s + kStagesB - 1 < KT) issue((s + kStagesB - 1) % kStagesB, s + kStagesB - 1);
     const uint8_t* st = smem + (s % kStagesB) * kStageB;
     if (my_mt > 0 && my_nt > 0) {
+      // K half 0's fragments, then half 1's reads in flight under half 0's MFMAs
       bf16x8 fa[2][2], fb[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      auto read_half = [&](int h) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) fa[h][t] = frag_mn(st, h, wm * 64 + t * 32, lane);
 #pragma unroll
@@ -221,20 +221,29 @@ __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a)
           if (kRK) fb[h][j] = frag_mn(st + kOpBytes, h, wn * 128 + j * 32, lane);
           else fb[h][j] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 128 + j * 32 + l32, h * 2 + hl));
         }
-      }
-      // the transposed reads land before any MFMA reads a fragment: the wait
-      // names every fragment as an operand, so no use can move above it
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fb[0][0]),
-                     "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3]), "+v"(fb[1][0]), "+v"(fb[1][1]),
-                     "+v"(fb[1][2]), "+v"(fb[1][3]));
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
+      };
+      // the transposed reads of half h land before any MFMA reads its
+      // fragments: the wait names them as operands, so no use moves above it
+      auto wait_half = [&](int h) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(fa[h][0]), "+v"(fa[h][1]), "+v"(fb[h][0]), "+v"(fb[h][1]), "+v"(fb[h][2]),
+                       "+v"(fb[h][3]));
+      };
+      auto mfma_half = [&](int h) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             if (j < my_nt && t < my_mt) acc[t][j] = mfma_bf16(fa[h][t], fb[h][j], acc[t][j]);
+      };
+      read_half(0);
+      wait_half(0);
+      read_half(1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_half(1);
+      mfma_half(1);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
