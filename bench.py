@@ -238,11 +238,14 @@ def bench_backward(args, s, L, dev):
     total_flops = 16.0 * P * s.H * s.I
     log("backward: %.3f ms/step, %.0f tokens/s, %.1f TFLOP/s over the expert GEMMs (recompute included)"
         % (ms_per_step, value, total_flops / (ms_per_step / 1e3) / 1e12))
+    kname = {"bwd_data": "gemm_bwd_kernel<0, false>", "bwd_weight": "gemm_bwd_kernel<1, false>",
+             "bwd_recompute": "gemm_bf16_kernel<0, false>"}[dom]
+    traffic = recorded_traffic(s.name + "_backward", kname)
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None,
-            "kernel": {"bwd_data": "gemm_bwd_kernel<0> (data-gradient GEMMs)",
-                       "bwd_weight": "gemm_bwd_kernel<1> (weight-gradient GEMMs)",
-                       "bwd_recompute": "gemm_bf16_kernel<0, false> (recompute of g, u)"}[dom],
+            "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": kname + {"bwd_data": " (data-gradient GEMMs)", "bwd_weight": " (weight-gradient GEMMs)",
+                               "bwd_recompute": " (recompute of g, u)"}[dom],
             "avg_launch_us": round(per_launch_ms * 1e3, 2), "alg_flops_per_launch": flops_per_launch}
     cpu = None
     if not args.no_cpu_baseline:
@@ -422,7 +425,7 @@ def main():
         flops = 2.0 * P * s.H * 2 * s.I
         achieved = flops / (avg_ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[s.experts]
-        kname = "gemm_packed_kernel<%s, 0, false>" % ("true" if s.experts == "fp8" else "false")
+        kname = "gemm_packed_kernel<%d, 0, false>" % {"bf16": 0, "fp8": 1, "fp4": 2}.get(s.experts, 0)
         traffic = recorded_traffic(s.name, kname) if layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),

@@ -845,7 +845,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.out = bw.ev;
     g.ldo = I;
     g.out_f32 = 1;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 0, grid_for(se.capacity), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, 0, grid_for(se.capacity), st), "backward GEMM launch");
   }
   {
     StageTimer tm(MOE_STAGE_BWD_MISC, st);
@@ -871,7 +871,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.out = bw.dxp;
     g.ldo = H;
     g.out_f32 = 1;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 0, grid_for(sdx.capacity), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, 0, grid_for(sdx.capacity), st), "backward GEMM launch");
   }
   {
     // dW_down[e] = sum over the expert's rows of dout (w a)^T
@@ -888,9 +888,12 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.out = dw_down;
     g.ldo = I;
     g.o_gs = (int64_t)H * I;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * bwd_tiles(I) * bwd_tiles(H), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, 0, E * bwd_tiles(I) * bwd_tiles(H), st), "backward GEMM launch");
+  }
+  {
     // dW_gate[e], dW_up[e] = sum over the expert's rows of [dg | du] x^T
-    g = BwdGemmArgs{};
+    StageTimer tm(MOE_STAGE_BWD_WEIGHT, st);
+    BwdGemmArgs g{};
     g.a = bw.x_sorted;
     g.lda = H;
     g.b = bw.dgu;
@@ -904,7 +907,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.n_split = I;
     g.ldo = H;
     g.o_gs = (int64_t)I * H;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, E * bwd_tiles(H) * bwd_tiles(2 * I), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, 0, E * bwd_tiles(H) * bwd_tiles(2 * I), st), "backward GEMM launch");
   }
   {
     // router: key gradients, dW_r = dkey^T x, dbias, and dkey . W_r into dx
@@ -930,7 +933,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.ldo = H;
     g.o_gs = (int64_t)E * H;
     g.out_f32 = 1;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 1, chunks * bwd_tiles(H) * bwd_tiles(Epad), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 1, 1, chunks * bwd_tiles(H) * bwd_tiles(Epad), st), "backward GEMM launch");
     MOE_TRY_HIP(launch_chunk_sum(bw.dwr_part, chunks, (int64_t)E * H, (uint16_t*)dw_router, st), "sum launch");
     g = BwdGemmArgs{};
     g.a = (const uint16_t*)w_router;
@@ -945,7 +948,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
     g.out = bw.dxr;
     g.ldo = H;
     g.out_f32 = 1;
-    MOE_TRY_HIP(launch_gemm_bwd(g, 0, bwd_tiles(d->T) * bwd_tiles(H), st), "backward GEMM launch");
+    MOE_TRY_HIP(launch_gemm_bwd(g, 0, 1, bwd_tiles(d->T) * bwd_tiles(H), st), "backward GEMM launch");
   }
   {
     StageTimer tm(MOE_STAGE_BWD_MISC, st);

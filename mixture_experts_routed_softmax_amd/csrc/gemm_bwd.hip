@@ -83,7 +83,9 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint8_t* st, int h, int m0, int 
   return __builtin_bit_cast(bf16x8, v8s{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
 }
 
-template <int kRK>
+// kRK: ragged K (weight gradients) or ragged rows (data gradients).  kRouter
+// only separates the router's launches from the experts' in profiles.
+template <int kRK, bool kRouter>
 __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStagesB * kStageB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -465,10 +467,13 @@ __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
 
 }  // namespace
 
-hipError_t launch_gemm_bwd(const BwdGemmArgs& a, int ragged_k, int grid, hipStream_t stream) {
+hipError_t launch_gemm_bwd(const BwdGemmArgs& a, int ragged_k, int router, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (ragged_k) hipLaunchKernelGGL(gemm_bwd_kernel<1>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
-  else hipLaunchKernelGGL(gemm_bwd_kernel<0>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  dim3 g(grid), b(kBwdThreads);
+  if (ragged_k && router) hipLaunchKernelGGL((gemm_bwd_kernel<1, true>), g, b, 0, stream, a);
+  else if (ragged_k) hipLaunchKernelGGL((gemm_bwd_kernel<1, false>), g, b, 0, stream, a);
+  else if (router) hipLaunchKernelGGL((gemm_bwd_kernel<0, true>), g, b, 0, stream, a);
+  else hipLaunchKernelGGL((gemm_bwd_kernel<0, false>), g, b, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -165,7 +165,8 @@ struct BwdGemmArgs {
   int out_f32;
   int k_chunk;
 };
-hipError_t launch_gemm_bwd(const BwdGemmArgs& a, int ragged_k, int grid, hipStream_t stream);
+// router: the router's two GEMMs (a separate instantiation, same code)
+hipError_t launch_gemm_bwd(const BwdGemmArgs& a, int ragged_k, int router, int grid, hipStream_t stream);
 hipError_t launch_swiglu_bwd(const float* ev, const float* gu, const int32_t* perm, const float* w, int64_t P,
                              int I, int act, float* dw, uint16_t* ap, uint16_t* dgu, hipStream_t stream);
 hipError_t launch_router_bwd(const float* part, int slices, int64_t T, int E, int Epad, const float* bias,
