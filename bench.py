@@ -56,7 +56,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="qwen_prefill",
-                   choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8", "dsv3_fp4"])
+                   choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8", "dsv3_fp4",
+                            "dsv3_ep8_shard"])
     p.add_argument("--T", type=int, default=None)
     p.add_argument("--scale-fmt", default="f32", choices=["f32", "ue8m0"])
     p.add_argument("--gate", default="silu", choices=["silu", "gelu", "relu"],

@@ -15,6 +15,8 @@ qwen_prefill   4096       2048   1408   60   4  bf16    softmax, no renorm, Zipf
 qwen_decode    1/8/32/64  2048   1408   60   4  bf16    softmax, no renorm, zero bias
 dsv3_bf16      8192       7168   2048   256  8  bf16    sigmoid, renorm, x2.5, Zipf bias
 dsv3_fp8       64/8192    7168   2048   256  8  e4m3    as dsv3_bf16; 128x128 block scales
+dsv3_fp4       64/8192    7168   2048   256  8  e2m1    as dsv3_bf16; UE8M0 per row per 32
+dsv3_ep8_shard 8192       7168   2048   32   8  bf16    sigmoid, renorm, x2.5, zero bias
 =============  =========  =====  =====  ===  =  ======  =============================
 
 Router inputs are snapped to grids so that every router logit is an exact fp32
@@ -86,6 +88,10 @@ _BASE = {
     # row per 32 K; activations fp8 per row per 128)
     "dsv3_fp4": LayerSpec("dsv3_fp4", 8192, 7168, 2048, 256, 8, "bf16", "fp4", "sigmoid",
                           True, 2.5, "zipf", "ue8m0"),
+    # one GPU's share of an 8-way expert-parallel DeepSeek-like layer: 32 local
+    # experts, 8 of them per token, so each expert receives about 2048 rows
+    "dsv3_ep8_shard": LayerSpec("dsv3_ep8_shard", 8192, 7168, 2048, 32, 8, "bf16", "bf16", "sigmoid",
+                                True, 2.5, "zero"),
 }
 
 # token counts each workload is exercised at
@@ -96,6 +102,7 @@ TOKEN_COUNTS = {
     "dsv3_bf16": (8192,),
     "dsv3_fp8": (64, 8192),
     "dsv3_fp4": (64, 8192),
+    "dsv3_ep8_shard": (8192,),
 }
 
 
