@@ -184,12 +184,12 @@ int64_t sched_capacity(const moe_desc* d, int ntiles) {
 
 // Weight streaming: work units (items x K splits) the launch must cover, and
 // split-K partial tiles the workspace must hold.  A split happens only below
-// kStreamTarget items, so split units stay below 2 * kStreamTarget.
-int64_t stream_units_cap(int64_t items) { return items + kStreamTarget; }
+// kStreamTarget items, so split units stay below 3 * kStreamTarget.
+int64_t stream_units_cap(int64_t items) { return 2 * items + kStreamTarget; }
 int64_t stream_partial_units(const moe_desc* d) {
   if (!use_stream(d)) return 0;
   const int64_t items = std::max(sched_capacity(d, gate_up_ntiles(d)), sched_capacity(d, down_ntiles(d)));
-  return std::min<int64_t>(items * kStreamMaxSplit, 2 * kStreamTarget);
+  return std::min<int64_t>(items * kStreamMaxSplit, 3 * kStreamTarget);
 }
 size_t stream_partial_bytes(const moe_desc* d) { return (size_t)stream_partial_units(d) * kStreamPartFloats * 4; }
 

@@ -107,17 +107,28 @@ hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, i
 constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamMaxScaleBlocks = 64;   // fp8 streaming: K / 128 at most (K <= 8192)
 constexpr int kStreamTarget = 1024;      // work units the split aims for (two rounds of 2 per CU)
+constexpr int kStreamSlots = 512;        // workgroups resident at once (256 CUs x 2)
 constexpr int kStreamMaxSplit = 16;
 constexpr int kStreamMinSteps = 4;       // K steps per split at least
 constexpr int kStreamPartFloats = 2 * 2 * 16 * 256;   // fp32 partial tile of one work unit
-// K splits per work item for `items` items of KT steps (host and device agree)
+// K splits per work item for `items` items of KT steps (host and device agree):
+// about kStreamTarget units, or one split more when that fills the last round
+// of kStreamSlots resident workgroups clearly better.  Units stay below
+// kStreamTarget + 2 * items.
 __host__ __device__ inline int stream_splits(int items, int KT) {
   if (items <= 0 || items >= kStreamTarget) return 1;
   int smax = KT / kStreamMinSteps;
   smax = smax < kStreamMaxSplit ? smax : kStreamMaxSplit;
   smax = smax < 1 ? 1 : smax;
-  const int s = (kStreamTarget + items - 1) / items;
-  return s < smax ? s : smax;
+  int s = (kStreamTarget + items - 1) / items;
+  s = s < smax ? s : smax;
+  if (s + 1 <= smax) {
+    const int u0 = items * s, u1 = items * (s + 1);
+    const int r0 = (u0 + kStreamSlots - 1) / kStreamSlots, r1 = (u1 + kStreamSlots - 1) / kStreamSlots;
+    // fill(s) = u / (rounds * slots); take s + 1 if it fills at least 5 points better
+    if ((int64_t)u1 * r0 * 100 >= (int64_t)u0 * r1 * 105) s = s + 1;
+  }
+  return s;
 }
 constexpr int kPackedTokBf16 = 256;          // token rows per packed bf16 tile
 constexpr int kPackedTokFp8 = 128;           // token rows per packed fp8 tile
