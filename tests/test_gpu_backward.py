@@ -110,11 +110,9 @@ def test_backward_is_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
-def test_backward_qwen_prefill_full_sampled():
-    """Full Qwen-like prefill shape (T=4096, 60 experts, k=4): dx on sampled
-    tokens, weight-gradient rows of the least-loaded, the median and the
-    75th-percentile expert."""
-    s = synthetic.spec("qwen_prefill")
+def _full_sampled(s, quantiles):
+    """dx on sampled tokens and weight-gradient rows of experts picked by load
+    quantile, at a full workload shape."""
     L = synthetic.make_layer(s, seed=0, device="cuda")
     dout = synthetic.make_grad_out(s, seed=0, device="cuda")
     got = _run_gpu(s, L, dout)
@@ -130,13 +128,26 @@ def test_backward_qwen_prefill_full_sampled():
     assert row_rel_err(_f64(got["dx"])[tokens], dx) <= TOL
     counts = np.bincount(ids.ravel(), minlength=s.E)
     order = np.argsort(counts, kind="stable")
-    for e in (int(order[np.nonzero(counts[order])[0][0]]), int(order[s.E // 2]), int(order[(3 * s.E) // 4])):
+    live = order[np.nonzero(counts[order])[0]]
+    for e in sorted({int(live[min(int(q * len(live)), len(live) - 1)]) for q in quantiles}):
         for which, name, nrows in ((oracle.BWD_GATE, "dw_gate", s.I), (oracle.BWD_UP, "dw_up", s.I),
                                    (oracle.BWD_DOWN, "dw_down", s.H)):
             rows = np.array([0, nrows - 1, int(rng.integers(nrows))])
             ref = oracle.bwd_expert_rows(ex, which, e, rows, hl["x"], ids, w, dout64)
             err = row_rel_err(_f64(got[name])[e][rows], ref)
             assert err <= TOL, (name, e, err)
+
+
+def test_backward_qwen_prefill_full_sampled():
+    """Full Qwen-like prefill shape (T=4096, 60 experts, k=4, softmax): the
+    least-loaded, the median and the 75th-percentile expert."""
+    _full_sampled(synthetic.spec("qwen_prefill"), (0.0, 0.5, 0.75))
+
+
+def test_backward_dsv3_full_sampled():
+    """Full DeepSeek-like shape (T=8192, H=7168, 256 experts, k=8, sigmoid,
+    renormalised x2.5): the least-loaded and the median expert."""
+    _full_sampled(synthetic.spec("dsv3_bf16"), (0.0, 0.5))
 
 
 def test_backward_no_tokens_zero_fills():
