@@ -20,7 +20,8 @@
 // pieces addressed by lanes 4j + i / 4 (j = 0..3), so lanes that address four
 // consecutive K rows at four consecutive 4-column pieces produce the
 // transposed 4 x 16 block.  Two such reads form the 8 K values a lane of
-// v_mfma_f32_32x32x16_bf16 needs.
+// v_mfma_f32_32x32x16_bf16 needs.  The reads are inline assembly followed by
+// one explicit lgkmcnt wait per K half (see frag_mn).
 //
 // Tile 256 (M) x 256 (N), K step 32, 8 waves of 64 x 128 (2 x 4 MFMA tiles),
 // 4 LDS stages of 32 KB (one workgroup per CU).  MN-major stages hold 32 K
@@ -45,7 +46,6 @@ constexpr int kLoadsB = 4;                     // DMA instructions per thread pe
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4s* lds_v4s;
 typedef __attribute__((address_space(3))) void* lds_void;
 
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
