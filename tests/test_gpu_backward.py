@@ -29,6 +29,7 @@ SMALL = {
     "idle_experts": dict(base="qwen_prefill", T=9, H=128, I=128, E=40, k=2),
     "one_token": dict(base="dsv3_bf16", T=1, H=128, I=256, E=8, k=3),
     "many_rows": dict(base="dsv3_bf16", T=700, H=384, I=128, E=6, k=2),
+    "max_experts_topk": dict(base="dsv3_bf16", T=24, H=128, I=128, E=256, k=32),
 }
 
 

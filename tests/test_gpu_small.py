@@ -206,6 +206,37 @@ def test_all_tokens_on_one_expert():
     assert counts.cpu().tolist() == [0, 0, 0, 0, 0, 260, 0, 0]
 
 
+@pytest.mark.parametrize("layout", ["rowmajor", "packed"])
+def test_max_experts_and_topk(layout):
+    # the largest E and k the library takes (256 experts, 32 per token)
+    s = synthetic.spec("dsv3_bf16", T=40, H=128, I=128, E=256, k=32)
+    L, hl = _layer(s, seed=12)
+    _check_forward(s, L, hl, layout=layout)
+
+
+@pytest.mark.parametrize("T", [1024, 1025])
+def test_permutation_chunk_boundary(T):
+    # 1024 (token, slot) pairs run the one-workgroup permutation, 1025 the
+    # histogram / scan / scatter launches
+    s = synthetic.spec("qwen_prefill", T=T, H=128, I=128, E=12, k=1)
+    L, hl = _layer(s, seed=13)
+    ids_o, _ = oracle_route(s, hl)
+    _, offsets_o, perm_o, inv_o = oracle.permute(ids_o, s.E)
+    _check_forward(s, L, hl, layout="packed")
+    d = desc_for(s)
+    counts = torch.empty(s.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T, dtype=torch.int32, device="cuda")
+    ids = torch.from_numpy(ids_o).cuda()
+    ws = moe.workspace(d, moe.MOE_OP_PERMUTE)
+    moe.moe_permute(d, ids, None, counts, offsets, perm, inv, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(offsets.cpu().numpy(), offsets_o)
+    assert np.array_equal(perm.cpu().numpy(), perm_o)
+    assert np.array_equal(inv.cpu().numpy(), inv_o)
+
+
 def test_exact_ties_break_to_lowest_index():
     s = synthetic.spec("qwen_prefill", T=64, H=128, I=128, E=10, k=3, bias="none")
     L, hl = _layer(s, seed=9)
