@@ -345,7 +345,9 @@ int route_slices(int64_t T, int H, int E) {
     return (int)(sl < 1 ? 1 : sl);
   }
   const int64_t tiles = ((T + 31) / 32) * ((E + 31) / 32);
-  const int max_slices = (H / 16) / 4;   // at least one 16-deep step per wave
+  // at least one 16-deep step per wave, and at most 8 slices: more would
+  // shorten the logits launch less than they lengthen the top-k sums
+  const int max_slices = (H / 16) / 4 < 8 ? (H / 16) / 4 : 8;
   int64_t sl = (512 + tiles - 1) / tiles;
   if (sl > max_slices) sl = max_slices;
   return (int)(sl < 1 ? 1 : sl);
