@@ -728,19 +728,35 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
   int32_t* counts = counts_out ? counts_out : fw.counts;
   const int64_t P = pairs(d);
 
-  if (d->T > 0) {
-    StageTimer tm(MOE_STAGE_ROUTE, st);
-    MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, d->H, d->E, d->k, d->act_dtype == MOE_DT_BF16,
-                                  d->score, d->renormalize, d->routed_scale, ids, w, fw.route_part, st),
-                "router launch");
-  }
   SchedRequest sgu{}, sdn{};
   if (d->w_dtype != MOE_DT_F32) {
     sgu = sched_req(fw.sched_gu, d, gate_up_ntiles(d));
     sdn = sched_req(fw.sched_dn, d, down_ntiles(d));
   }
-  if ((s = run_permute(d, ids, counts, fw.offsets, fw.perm, fw.inv, fw.touched, fw.pw, sgu, sdn, st)) != MOE_OK)
-    return s;
+  // small bf16 batches: the top-k selection runs in the one-workgroup
+  // permutation launch, right after the logits
+  const bool select_in_permute = d->act_dtype == MOE_DT_BF16 && d->T > 0 && d->T <= kSelectPermuteMaxT &&
+                                 !route_big(d->T, d->H) && P <= kPermChunk;
+  if (select_in_permute) {
+    {
+      StageTimer tm(MOE_STAGE_ROUTE, st);
+      MOE_TRY_HIP(launch_route_logits(x, w_router, d->T, d->H, d->E, fw.route_part, st), "router launch");
+    }
+    StageTimer tm(MOE_STAGE_SCAN, st);
+    MOE_TRY_HIP(launch_select_permute_small(fw.route_part, route_slices(d->T, d->H, d->E), d->T, d->E, bias, d->k,
+                                            d->score, d->renormalize, d->routed_scale, ids, w, counts, fw.offsets,
+                                            fw.perm, fw.inv, fw.touched, sgu, sdn, st),
+                "selection and permute launch");
+  } else {
+    if (d->T > 0) {
+      StageTimer tm(MOE_STAGE_ROUTE, st);
+      MOE_TRY_HIP(launch_route_topk(x, w_router, bias, d->T, d->H, d->E, d->k, d->act_dtype == MOE_DT_BF16,
+                                    d->score, d->renormalize, d->routed_scale, ids, w, fw.route_part, st),
+                  "router launch");
+    }
+    if ((s = run_permute(d, ids, counts, fw.offsets, fw.perm, fw.inv, fw.touched, fw.pw, sgu, sdn, st)) != MOE_OK)
+      return s;
+  }
   if (P == 0) return MOE_OK;
   const void* act = x;
   const float* act_scales = nullptr;

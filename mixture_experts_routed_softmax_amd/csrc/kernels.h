@@ -14,6 +14,11 @@ hipError_t launch_route_topk(const void* x, const void* w_router, const float* b
                              int H, int E, int k, int act_bf16, int score, int renorm,
                              float routed_scale, int32_t* ids, float* w, float* part, hipStream_t stream);
 int route_slices(int64_t T, int H, int E);
+bool route_big(int64_t T, int H);
+// bf16 logits of a batch the small-batch router takes (!route_big): partial
+// sums of route_slices() K slices, part[slice][T][E]
+hipError_t launch_route_logits(const void* x, const void* w_router, int64_t T, int H, int E, float* part,
+                               hipStream_t stream);
 size_t route_workspace_bytes(int64_t T, int H, int E, int act_bf16);
 
 // ---- permutation
@@ -37,6 +42,14 @@ hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int3
                        SchedRequest s0, SchedRequest s1, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* block_base,
                           int32_t* perm, int32_t* inv, hipStream_t stream);
+// top-k selection of every token from the partial logits of
+// launch_route_logits, then hist + scan + scatter, in one workgroup, for
+// T <= kSelectPermuteMaxT and T * k <= kPermChunk
+constexpr int kSelectPermuteMaxT = 16;   // one token per wave: 32 tokens measured slower than two launches
+hipError_t launch_select_permute_small(const float* part, int slices, int64_t T, int E, const float* bias, int k,
+                                       int score, int renorm, float routed_scale, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                       int32_t* touched, SchedRequest s0, SchedRequest s1, hipStream_t stream);
 // hist + scan + scatter in one workgroup, for P <= kPermChunk
 hipError_t launch_permute_small(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* inv, int32_t* touched, SchedRequest s0, SchedRequest s1,
@@ -112,11 +125,16 @@ constexpr int kStreamMaxSplit = 16;
 constexpr int kStreamMinSteps = 4;       // K steps per split at least
 constexpr int kStreamPartFloats = 2 * 2 * 16 * 256;   // fp32 partial tile of one work unit
 // K splits per work item for `items` items of KT steps (host and device agree):
-// about kStreamTarget units, or one split more when that fills the last round
-// of kStreamSlots resident workgroups clearly better.  Units stay below
-// kStreamTarget + 2 * items.
+// none when the items alone fill at least 90% of their rounds of
+// kStreamSlots resident workgroups (a split would only add the partial-tile
+// traffic and the reduction); else about kStreamTarget units, or one split
+// more when that fills the last round clearly better.  Units stay below
+// kStreamTarget + 2 * items.  Every workgroup evaluates this at its start, so
+// it stays free of loops and variable divisions.
 __host__ __device__ inline int stream_splits(int items, int KT) {
   if (items <= 0 || items >= kStreamTarget) return 1;
+  const int r1 = (items + kStreamSlots - 1) / kStreamSlots;
+  if (items * 10 >= r1 * kStreamSlots * 9) return 1;
   int smax = KT / kStreamMinSteps;
   smax = smax < kStreamMaxSplit ? smax : kStreamMaxSplit;
   smax = smax < 1 ? 1 : smax;
@@ -124,9 +142,9 @@ __host__ __device__ inline int stream_splits(int items, int KT) {
   s = s < smax ? s : smax;
   if (s + 1 <= smax) {
     const int u0 = items * s, u1 = items * (s + 1);
-    const int r0 = (u0 + kStreamSlots - 1) / kStreamSlots, r1 = (u1 + kStreamSlots - 1) / kStreamSlots;
+    const int r0 = (u0 + kStreamSlots - 1) / kStreamSlots, r1b = (u1 + kStreamSlots - 1) / kStreamSlots;
     // fill(s) = u / (rounds * slots); take s + 1 if it fills at least 5 points better
-    if ((int64_t)u1 * r0 * 100 >= (int64_t)u0 * r1 * 105) s = s + 1;
+    if ((int64_t)u1 * r0 * 100 >= (int64_t)u0 * r1b * 105) s = s + 1;
   }
   return s;
 }

@@ -16,6 +16,7 @@
 // or, when all pairs fit one chunk, a single workgroup that does all three.
 #include "common.h"
 #include "kernels.h"
+#include "topk_select.h"
 
 namespace moe {
 
@@ -161,10 +162,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(
 // All of the above in one workgroup when the pairs fit one chunk (P <= 1024,
 // e.g. decode batches): histogram, counts and offsets, stable ranks, the
 // touched-expert list and the schedules, with a single launch.
-__global__ __launch_bounds__(1024) void permute_small_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ touched, SchedRequest s0,
-    SchedRequest s1) {
+// Body of the one-workgroup permutation (1024 threads): thread p < P holds the
+// expert e of pair p (-1 for none).
+__device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                   int32_t* __restrict__ touched, SchedRequest s0, SchedRequest s1) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_wcount[16][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
@@ -175,7 +177,6 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   for (int x = tid; x < E; x += 1024) s_cnt[x] = 0;
   for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
   __syncthreads();
-  int e = tid < P ? ids[tid] : -1;
   if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
   // rank among earlier lanes of this wave with the same expert
   int rank = 0;
@@ -213,6 +214,38 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   }
   if (s0.sched != nullptr) build_schedule(s_offsets, E, s0, s_tiles, s_items, s_tmp);
   if (s1.sched != nullptr) build_schedule(s_offsets, E, s1, s_tiles, s_items, s_tmp);
+}
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ touched, SchedRequest s0,
+    SchedRequest s1) {
+  const int tid = threadIdx.x;
+  permute_small_body(tid < P ? ids[tid] : -1, P, E, counts, offsets, perm, inv, touched, s0, s1);
+}
+
+// Small batches (T <= kSelectPermuteMaxT = 16, T * k <= 1024): the top-k selection
+// of every token (wave w selects tokens w, w + 16, ..., exactly as the
+// router's selection launch does) and the permutation of the selected pairs
+// in one workgroup; the ids reach the permutation through LDS.
+__global__ __launch_bounds__(1024) void select_permute_small_kernel(
+    const float* __restrict__ part, int slices, int T, int E, const float* __restrict__ bias, int k, int score,
+    int renorm, float routed_scale, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ touched, SchedRequest s0, SchedRequest s1) {
+  __shared__ int s_ids[kPermChunk];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int tok = wave; tok < T; tok += 16) {
+    float key[4];
+    bool taken[4];
+    token_keys(part, slices, T, tok, E, bias, lane, key, taken);
+    select_topk(key, taken, lane, E, k, score, renorm, routed_scale, ids_out + (int64_t)tok * k,
+                w_out + (int64_t)tok * k, s_ids + tok * k);
+  }
+  __syncthreads();
+  const int P = T * k, tid = threadIdx.x;
+  permute_small_body(tid < P ? s_ids[tid] : -1, P, E, counts, offsets, perm, inv, touched, s0, s1);
 }
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
@@ -335,6 +368,17 @@ hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* b
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(256), 0, stream, ids, P, E,
                      block_base, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_permute_small(const float* part, int slices, int64_t T, int E, const float* bias, int k,
+                                       int score, int renorm, float routed_scale, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                       int32_t* touched, SchedRequest s0, SchedRequest s1, hipStream_t stream) {
+  if (T <= 0 || T > kSelectPermuteMaxT || T * k > kPermChunk || E > kMaxExperts || k > 64)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(select_permute_small_kernel, dim3(1), dim3(1024), 0, stream, part, slices, (int)T, E, bias, k,
+                     score, renorm, routed_scale, ids, w, counts, offsets, perm, inv, touched, s0, s1);
   return hipGetLastError();
 }
 

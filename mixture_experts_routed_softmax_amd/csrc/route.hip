@@ -16,69 +16,13 @@
 // rounds of a 64-lane argmax reduction.
 #include "common.h"
 #include "kernels.h"
+#include "topk_select.h"
 
 namespace moe {
 
 namespace {
 
 constexpr int kTokPerBlock = 32;
-
-struct KeyIdx {
-  float key;
-  int idx;
-};
-
-__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
-// Top-k of one token's keys held by a wave (lane l owns experts l, l+64,
-// l+128, l+192): k rounds of a 64-lane argmax (larger key wins, ties to the
-// lower index), then the scores and routing weights; lane i < k writes slot i.
-__device__ __forceinline__ void select_topk(float (&key)[4], bool (&taken)[4], int lane, int E, int k, int score,
-                                            int renorm, float routed_scale, int32_t* ids_out, float* w_out) {
-  float my_key = 0.f;   // lane i < k keeps slot i
-  int my_idx = 0;
-  float kmax = 0.f;
-  for (int i = 0; i < k; ++i) {
-    float bk = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (!taken[q] && better(key[q], lane + 64 * q, bk, bi)) { bk = key[q]; bi = lane + 64 * q; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ok = __shfl_xor(bk, off);
-      int oi = __shfl_xor(bi, off);
-      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
-    }
-    if ((bi & 63) == lane) taken[bi >> 6] = true;
-    if (lane == i) { my_key = bk; my_idx = bi; }
-    if (i == 0) kmax = bk;
-  }
-  float s;
-  if (score == 0) {  // softmax over all experts
-    float part = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + 64 * q < E) part += expf(key[q] - kmax);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    s = expf(my_key - kmax) / part;
-  } else {
-    s = 1.0f / (1.0f + expf(-my_key));
-  }
-  if (renorm) {
-    float sum = lane < k ? s : 0.f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    s = s / sum;
-  }
-  if (lane < k) {
-    ids_out[lane] = my_idx;
-    w_out[lane] = s * routed_scale;
-  }
-}
 
 // fp32 router (small fp32 layers): one workgroup owns 32 tokens and all
 // experts, logits by fp32 FMA into LDS, then the wave-level selection.
@@ -304,29 +248,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   if (tok >= T) return;
   float key[4];
   bool taken[4];
-  // Slices are added in ascending order; the loads of 8 slices are issued
-  // together so that their latencies overlap.
-  float z[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int sl0 = 0; sl0 < slices; sl0 += 8) {
-    float v[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[q][u] = (e < E && sl0 + u < slices) ? part[((int64_t)(sl0 + u) * T + tok) * E + e] : 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) z[q] += v[q][u];
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    taken[q] = !(e < E);
-    key[q] = e < E ? z[q] + (bias ? bias[e] : 0.f) : -INFINITY;
-  }
+  token_keys(part, slices, T, tok, E, bias, lane, key, taken);
   select_topk(key, taken, lane, E, k, score, renorm, routed_scale, ids_out + tok * k, w_out + tok * k);
 }
 
@@ -358,6 +280,19 @@ size_t route_workspace_bytes(int64_t T, int H, int E, int act_bf16) {
   return (size_t)route_slices(T, H, E) * T * E * sizeof(float);
 }
 
+hipError_t launch_route_logits(const void* x, const void* w_router, int64_t T, int H, int E, float* part,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (route_big(T, H)) return hipErrorInvalidValue;
+  const int slices = route_slices(T, H, E);
+  const int nsteps = H / 16;
+  const int per = (nsteps + slices - 1) / slices;
+  dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 31) / 32), (unsigned)slices);
+  hipLaunchKernelGGL(logits_kernel, grid, dim3(256), 0, stream, (const uint16_t*)x, (const uint16_t*)w_router, T, H,
+                     E, per, part);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_topk(const void* x, const void* w_router, const float* bias, int64_t T,
                              int H, int E, int k, int act_bf16, int score, int renorm,
                              float routed_scale, int32_t* ids, float* w, float* part, hipStream_t stream) {
@@ -379,16 +314,10 @@ hipError_t launch_route_topk(const void* x, const void* w_router, const float* b
     return hipGetLastError();
   }
   if (act_bf16) {
-    const int slices = route_slices(T, H, E);
-    const int nsteps = H / 16;
-    const int per = (nsteps + slices - 1) / slices;
-    dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 31) / 32), (unsigned)slices);
-    hipLaunchKernelGGL(logits_kernel, grid, dim3(256), 0, stream, (const uint16_t*)x, (const uint16_t*)w_router,
-                       T, H, E, per, part);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_route_logits(x, w_router, T, H, E, part, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, part, slices, T, E, bias,
-                       k, score, renorm, routed_scale, ids, w);
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, part,
+                       route_slices(T, H, E), T, E, bias, k, score, renorm, routed_scale, ids, w);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((T + kTokPerBlock - 1) / kTokPerBlock));

@@ -237,8 +237,20 @@ def test_permutation_chunk_boundary(T):
     assert np.array_equal(inv.cpu().numpy(), inv_o)
 
 
-def test_exact_ties_break_to_lowest_index():
-    s = synthetic.spec("qwen_prefill", T=64, H=128, I=128, E=10, k=3, bias="none")
+@pytest.mark.parametrize("T,k", [(1, 8), (16, 4), (16, 32), (17, 4), (32, 32)])
+def test_small_batch_selection_in_permute(T, k):
+    """Batches of at most 16 tokens select their experts inside the
+    one-workgroup permutation launch (17 or more take the separate selection
+    launch); ids, weights, counts and outputs must match the oracle on both
+    sides of the boundary, with up to 32 experts per token."""
+    s = synthetic.spec("dsv3_bf16", T=T, H=256, I=128, E=64, k=k)
+    L, hl = _layer(s, seed=21)
+    _check_forward(s, L, hl, layout="packed")
+
+
+@pytest.mark.parametrize("T", [16, 64])
+def test_exact_ties_break_to_lowest_index(T):
+    s = synthetic.spec("qwen_prefill", T=T, H=128, I=128, E=10, k=3, bias="none")
     L, hl = _layer(s, seed=9)
     for dup in (4, 7, 9):
         L["w_router"][dup] = L["w_router"][2]
