@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <algorithm>
 #include <vector>
 
 #include "moe.h"
@@ -314,20 +315,39 @@ hipEvent_t pool_event() {
   return e;
 }
 
+// Within one library call the launches are timed back to back: a stage's
+// start event is the previous stage's stop event on the same stream (one
+// event per launch instead of two; nothing else is enqueued in between).
+// Every entry point resets the chain, so work enqueued between calls is never
+// attributed to a stage.  The gate/up and backward weight-gradient stages
+// (the dominant GEMMs) keep a start event of their own, recorded right before
+// their launch: a chained start also counts the dispatch gap before the
+// launch (measured: qwen_prefill gate/up 292 instead of 285 us, against a
+// 284.5 us kernel).
+hipEvent_t g_chain = nullptr;
+hipStream_t g_chain_stream = nullptr;
+
 struct StageTimer {
   int stage;
   hipStream_t s;
   hipEvent_t a = nullptr, b = nullptr;
   StageTimer(int st, hipStream_t stream) : stage(st), s(stream) {
     if (!g_timing) return;
-    a = pool_event();
+    const bool own_start = st == MOE_STAGE_GATE_UP || st == MOE_STAGE_BWD_WEIGHT;
+    if (g_chain && g_chain_stream == s && !own_start) {
+      a = g_chain;
+    } else {
+      a = pool_event();
+      if (a) hipEventRecord(a, s);
+    }
     b = pool_event();
-    if (a && b) hipEventRecord(a, s);
   }
   ~StageTimer() {
     if (!g_timing || !a || !b) return;
     hipEventRecord(b, s);
     g_pending.push_back({stage, a, b});
+    g_chain = b;
+    g_chain_stream = s;
   }
 };
 
@@ -591,6 +611,7 @@ size_t moe_workspace_bytes(const moe_desc* d, int op) {
 moe_status moe_route_topk(const moe_desc* d, const void* x, const void* w_router, const float* bias,
                           int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (d->T == 0) return MOE_OK;
@@ -609,6 +630,7 @@ moe_status moe_permute(const moe_desc* d, const int32_t* ids, const void* x, int
                        int32_t* offsets, int32_t* perm, int32_t* inv, void* x_sorted,
                        float* x_sorted_scales, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (!counts || !offsets) return fail(MOE_EINVAL, "counts and offsets are required");
@@ -646,6 +668,7 @@ moe_status moe_expert_gate_up_swiglu(const moe_desc* d, const void* x_sorted, co
                                      const void* w_gate_scales, const void* w_up_scales, void* h,
                                      float* h_scales, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (pairs(d) == 0) return MOE_OK;
@@ -670,6 +693,7 @@ moe_status moe_expert_down(const moe_desc* d, const void* h, const float* h_scal
                            const void* w_down, const void* w_down_scales, void* y_sorted, void* ws,
                            size_t ws_bytes, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (pairs(d) == 0) return MOE_OK;
@@ -691,6 +715,7 @@ moe_status moe_expert_down(const moe_desc* d, const void* h, const float* h_scal
 moe_status moe_unpermute_combine(const moe_desc* d, const void* y_sorted, const int32_t* inv,
                                  const float* topk_w, void* out, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (d->T == 0) return MOE_OK;
@@ -709,6 +734,7 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
                        const void* su, const void* sd, void* out, int32_t* ids_out, float* w_out,
                        int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if ((s = check_ws(d, MOE_OP_FORWARD, ws, ws_bytes)) != MOE_OK) return s;
@@ -784,6 +810,7 @@ moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router,
                         void* dw_router, float* d_bias, void* dw_gate, void* dw_up, void* dw_down, void* ws,
                         size_t ws_bytes, void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate_backward(d0);
   if (s != MOE_OK) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -982,6 +1009,7 @@ size_t moe_packed_weight_bytes(const moe_desc* d, int which) {
 moe_status moe_pack_weights(const moe_desc* d, int which, const void* w0, const void* w1, void* dst,
                             void* stream) {
   g_err.clear();
+  g_chain = nullptr;
   moe_status s = validate(d);
   if (s != MOE_OK) return s;
   if (d->w_dtype == MOE_DT_F32) return fail(MOE_EUNSUPPORTED, "packed weights are bf16 or fp8");
@@ -1014,10 +1042,18 @@ moe_status moe_timing_read(double* ms, int64_t* launches) {
       result = fail(MOE_EHIP, "event timing failed");
     ms[p.stage] += t;
     launches[p.stage] += 1;
-    g_event_pool.push_back(p.start);
-    g_event_pool.push_back(p.stop);
   }
+  // chained launches share events: return each one to the pool once
+  std::vector<hipEvent_t> used;
+  for (auto& p : g_pending) {
+    used.push_back(p.start);
+    used.push_back(p.stop);
+  }
+  std::sort(used.begin(), used.end());
+  used.erase(std::unique(used.begin(), used.end()), used.end());
+  for (hipEvent_t e : used) g_event_pool.push_back(e);
   g_pending.clear();
+  g_chain = nullptr;
   return result;
 }
 

@@ -378,3 +378,28 @@ def test_gated_activation_variants(gate, name, layout, path):
     err = row_rel_err(out.cpu().float().numpy(), out_o)
     print("%s %s %s %s: max row rel err %.3e" % (gate, name, layout, path, err))
     assert err <= tol_of(s)
+
+
+def test_stage_timing_counts_every_launch():
+    """Stage timing: every launch of a forward is counted once under its
+    stage with a positive duration (launches of one call are timed back to
+    back), and the stage times of a call add up to no more than its wall time."""
+    s = SMALL["bf16_softmax"]            # 1200 pairs: the three-launch permutation
+    L, _ = _layer(s)
+    run_forward(s, L, layout="packed")
+    torch.cuda.synchronize()
+    moe.moe_timing_enable(True)
+    moe.moe_timing_read()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(3):
+        run_forward(s, L, layout="packed")
+    stop.record()
+    torch.cuda.synchronize()
+    st = moe.moe_timing_read()
+    moe.moe_timing_enable(False)
+    for name in ("route", "hist", "scan", "scatter", "gate_up", "down", "combine"):
+        ms, n = st[name]
+        assert n == 3 and ms > 0, (name, ms, n)
+    assert sum(ms for ms, _ in st.values()) <= start.elapsed_time(stop) * 1.001
+    assert moe.moe_timing_read()["gate_up"][1] == 0
