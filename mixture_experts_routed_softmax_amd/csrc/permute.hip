@@ -121,9 +121,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   const int64_t per = (nblocks + 3) / 4;
   const int64_t b0 = part * per;
   const int64_t b1 = min(nblocks, b0 + per);
+  // the chunk counts are read 8 at a time so that their load latencies overlap
   int sum = 0;
   if (e < E)
-    for (int64_t b = b0; b < b1; ++b) sum += block_counts[b * E + e];
+    for (int64_t b = b0; b < b1; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? block_counts[(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += c[u];
+    }
   s_part[part][e] = sum;
   __syncthreads();
   if (tid < E) {
@@ -140,10 +147,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   if (e < E) {
     int run = s_offsets[e];
     for (int p = 0; p < part; ++p) run += s_part[p][e];
-    for (int64_t b = b0; b < b1; ++b) {
-      int c = block_counts[b * E + e];
-      block_base[b * E + e] = run;
-      run += c;
+    for (int64_t b = b0; b < b1; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? block_counts[(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b + u < b1) {
+          block_base[(b + u) * E + e] = run;
+          run += c[u];
+        }
     }
   }
   // touched experts, ascending, count in touched[E]
@@ -266,15 +279,23 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   __shared__ int s_cursor[kMaxExperts];
   __shared__ int s_wcount[4][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  // every round's ids are loaded first, together with the chunk's bases
+  int ids_r[kPermChunk / 256];
+#pragma unroll
+  for (int round = 0; round < kPermChunk / 256; ++round) {
+    const int64_t p = base + round * 256 + tid;
+    ids_r[round] = p < P ? ids[p] : -1;
+  }
   for (int e = tid; e < E; e += 256) {
     s_cursor[e] = block_base[(int64_t)blockIdx.x * E + e];
     s_wcount[0][e] = s_wcount[1][e] = s_wcount[2][e] = s_wcount[3][e] = 0;
   }
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kPermChunk;
+#pragma unroll
   for (int round = 0; round < kPermChunk / 256; ++round) {
     const int64_t p = base + round * 256 + tid;
-    int e = p < P ? ids[p] : -1;
+    int e = ids_r[round];
     if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
     const bool valid = e >= 0;
     // rank among earlier lanes of this wave with the same expert
