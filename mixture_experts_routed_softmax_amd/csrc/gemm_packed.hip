@@ -25,9 +25,11 @@
 //
 // Pipeline: an LDS ring of 32 KB (bf16: 16 KB weights + 16 KB tokens, 5
 // stages) or 24 KB (fp8, 6 stages) stages filled with global_load_lds_dwordx4
-// several K steps ahead; one barrier per step; the fragments of step s+1 are
-// read from LDS while the MFMAs of step s run.  Token rows are read through the expert permutation when a gather
-// index is given; token tiles past the expert's last row skip their MFMAs.
+// several K steps ahead (bf16, fp4: issued after the step's last MFMA); one
+// barrier per step; the fragments of step s+1 are read from LDS while the
+// MFMAs of step s run.  Token rows are read through the expert permutation
+// when a gather index is given; token tiles past the expert's last row skip
+// their MFMAs.
 //
 // FP8: per 128-deep K block (two steps) the MFMA partial sums are promoted
 // into the fp32 accumulators with s_w(block) * s_x(row, block); the gate/up
@@ -368,6 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     if (full_loads) wait_steps<kLoads>(ahead);
     else wait_steps<kLoads - 1>(ahead);
   };
+  constexpr bool kDmaLate = kW != kWFp8;
   auto mainloop = [&](auto nt_const) {
     constexpr int NT = decltype(nt_const)::value;
     constexpr std::integral_constant<int, 0> h0{};
@@ -384,7 +387,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     wait_lgkm<0>();
     // One K step: the MFMAs of step s, with the fragments of step s+1 read
     // from LDS stage `next` half by half as the MFMAs free their registers.
-    auto body = [&](int s, int next) {
+    // bf16 and fp4 issue the DMA of step fkt into stage fst (fkt < 0: none)
+    // after the last MFMA of the step: issued right after the barrier it
+    // delayed the MFMAs (gate/up: dsv3_bf16 4.85 -> 4.77 ms, expert-parallel
+    // shard 3.56 -> 3.43 ms, dsv3_fp4 3.98 -> 3.72 ms; issued between the two
+    // halves it was slower still).  fp8 (six stages, one MFMA per fragment
+    // half) keeps it right after the barrier: late, its gate/up took 5.12
+    // instead of 4.86 ms.
+    auto body = [&](int s, int next, int fst, int fkt) {
       __builtin_amdgcn_sched_barrier(0);
       // this step's first half landed (fp4: and the scales, read before the
       // second half's fragments, which may still be in flight)
@@ -395,6 +405,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       wait_lgkm<kFp4 ? 2 + 2 * NT : (kFp8 ? (NT >= 1 ? 2 : 0) : 2 + NT)>();   // ... and its second half
       mfma_half(f, h1, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      if (fkt >= 0) issue(fst, fkt);
       __builtin_amdgcn_sched_barrier(0);
       read_half(next, f, h1, nt_const);
       __builtin_amdgcn_sched_barrier(0);
@@ -408,10 +420,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     for (; s < KT - (kStages - 1); ++s) {
       const int next = stage + 1 == kStages ? 0 : stage + 1;
       wait_ahead(kStages - 3);                // step s+1 landed for this thread
-      __builtin_amdgcn_s_barrier();           // ... and for all; step s-1's stage is free
-      issue(fill, s + kStages - 1);
+      __builtin_amdgcn_s_barrier();           // ... and for all; step s-1's stage is free (refilled in body)
+      const int fst = fill;
       fill = fill + 1 == kStages ? 0 : fill + 1;
-      body(s, next);
+      if constexpr (kDmaLate) {
+        body(s, next, fst, s + kStages - 1);
+      } else {
+        issue(fst, s + kStages - 1);
+        body(s, next, 0, -1);
+      }
       stage = next;
     }
     // drain: nothing left to issue
@@ -419,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
       const int next = stage + 1 == kStages ? 0 : stage + 1;
       wait_ahead(KT - 2 - s);
       __builtin_amdgcn_s_barrier();
-      body(s, next);
+      body(s, next, 0, -1);
       stage = next;
     }
     mfma_half(f, h0, nt_const);
