@@ -424,7 +424,7 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
-                           (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), st);
+                           (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), d->T <= 32, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
@@ -453,7 +453,7 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
-                           (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), st);
+                           (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), d->T <= 32, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);

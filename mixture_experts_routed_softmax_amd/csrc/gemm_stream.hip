@@ -43,6 +43,12 @@ constexpr int kRing = kW == 0 ? 4 : (kW == 1 ? 3 : 5);   // K steps in flight pe
 // takes the whole register file with one wave per SIMD
 template <int kW>
 constexpr int kWavesPerSimd = kW == 2 ? 1 : 2;
+// batches of at most 32 tokens (one 32-token tile per item): without the
+// second token tile a bf16 workgroup fits three to a CU (fp8 would spill)
+template <int kW, bool kOneTile>
+constexpr int kBlocksPerCu = kOneTile && kW == 0 ? 3 : kWavesPerSimd<kW>;   // 0: bf16
+template <int kW, bool kOneTile>
+constexpr int kSlots = 256 * kBlocksPerCu<kW, kOneTile>;   // resident workgroups
 
 __device__ __forceinline__ int pswz(int row, int chunk) {
   return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -386,18 +392,18 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
 }
 
-template <int kW, int kMode, bool kOutF32>
-__global__ __launch_bounds__(256, kWavesPerSimd<kW>) void gemm_stream_kernel(GemmArgs a) {
+template <int kW, int kMode, bool kOutF32, bool kOneTile>
+__global__ __launch_bounds__(256, (kBlocksPerCu<kW, kOneTile>)) void gemm_stream_kernel(GemmArgs a) {
   const int items = a.sched->total;
   const int KT = stream_steps<kW>(a.K);
-  const int S = stream_splits(items, KT);
+  const int S = stream_splits(items, KT, kSlots<kW, kOneTile>);
   const int u = xcd_work_index(items * S);
   if (u < 0) return;
   const int w = u / S, sp = u - w * S;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
   const int kt0 = (int)((int64_t)KT * sp / S), kt1 = (int)((int64_t)KT * (sp + 1) / S);
   float* part = S > 1 ? a.partial + (int64_t)u * kStreamPartFloats : nullptr;
-  if (it.row_end - it.row_begin > 32)
+  if (!kOneTile && it.row_end - it.row_begin > 32)
     stream_tile<kW, kMode, kOutF32, 2>(a, it, kt0, kt1, part);
   else
     stream_tile<kW, kMode, kOutF32, 1>(a, it, kt0, kt1, part);
@@ -408,12 +414,12 @@ __global__ __launch_bounds__(256, kWavesPerSimd<kW>) void gemm_stream_kernel(Gem
 // Nothing to do when S == 1.  Partial tile layout: part[row * 256 + c] with,
 // for gate/up, the gate value of channel ntile*128 + w*32 + x at c = w*64 + x
 // and its up value at c = w*64 + 32 + x; for down, channel ntile*256 + c.
-template <int kW, int kMode, bool kOutF32>
+template <int kW, int kMode, bool kOutF32, bool kOneTile>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
   constexpr bool kFp8 = kW != kWBf16;   // fp8 activations and h (fp8 and fp4 weights)
   const int items = a.sched->total;
   const int KT = stream_steps<kW>(a.K);
-  const int S = stream_splits(items, KT);
+  const int S = stream_splits(items, KT, kSlots<kW, kOneTile>);
   const int w = blockIdx.x;
   if (S == 1 || w >= items) return;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
@@ -494,13 +500,19 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, hipStream_t stream) {
+hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, int one_tile,
+                              hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   dim3 g(grid), rg(reduce_grid), b(256);
-#define MOE_STREAM_LAUNCH(W, M, F32)                                                   \
+#define MOE_STREAM_LAUNCH_T(W, M, F32, ONE)                                            \
   do {                                                                                 \
-    hipLaunchKernelGGL((gemm_stream_kernel<W, M, F32>), g, b, 0, stream, a);           \
-    hipLaunchKernelGGL((stream_reduce_kernel<W, M, F32>), rg, b, 0, stream, a);        \
+    hipLaunchKernelGGL((gemm_stream_kernel<W, M, F32, ONE>), g, b, 0, stream, a);      \
+    hipLaunchKernelGGL((stream_reduce_kernel<W, M, F32, ONE>), rg, b, 0, stream, a);   \
+  } while (0)
+#define MOE_STREAM_LAUNCH(W, M, F32)                      \
+  do {                                                    \
+    if (one_tile) MOE_STREAM_LAUNCH_T(W, M, F32, true);   \
+    else MOE_STREAM_LAUNCH_T(W, M, F32, false);           \
   } while (0)
   if (wfmt == kWFp4) {
     if (mode == 0) MOE_STREAM_LAUNCH(kWFp4, 0, false);
@@ -516,6 +528,7 @@ hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, i
     else MOE_STREAM_LAUNCH(kWBf16, 1, false);
   }
 #undef MOE_STREAM_LAUNCH
+#undef MOE_STREAM_LAUNCH_T
   return hipGetLastError();
 }
 

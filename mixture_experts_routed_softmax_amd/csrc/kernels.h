@@ -116,7 +116,9 @@ constexpr int kPackedDownChannels = 256;     // output channels per packed down 
 // reduction launch (reduce_grid >= min(item capacity, kStreamTarget): only
 // fewer than kStreamTarget items are ever split)
 // wfmt: weight format, 0 bf16, 1 fp8, 2 fp4 (fp8 activations for 1 and 2)
-hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, hipStream_t stream);
+// one_tile: every expert holds at most 32 of the batch's rows (T <= 32)
+hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, int one_tile,
+                              hipStream_t stream);
 constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamMaxScaleBlocks = 64;   // fp8 streaming: K / 128 at most (K <= 8192)
 constexpr int kStreamTarget = 1024;      // work units the split aims for (two rounds of 2 per CU)
@@ -131,10 +133,10 @@ constexpr int kStreamPartFloats = 2 * 2 * 16 * 256;   // fp32 partial tile of on
 // more when that fills the last round clearly better.  Units stay below
 // kStreamTarget + 2 * items.  Every workgroup evaluates this at its start, so
 // it stays free of loops and variable divisions.
-__host__ __device__ inline int stream_splits(int items, int KT) {
+__host__ __device__ inline int stream_splits(int items, int KT, int slots = kStreamSlots) {
   if (items <= 0 || items >= kStreamTarget) return 1;
-  const int r1 = (items + kStreamSlots - 1) / kStreamSlots;
-  if (items * 10 >= r1 * kStreamSlots * 9) return 1;
+  const int r1 = (items + slots - 1) / slots;
+  if (items * 10 >= r1 * slots * 9) return 1;
   int smax = KT / kStreamMinSteps;
   smax = smax < kStreamMaxSplit ? smax : kStreamMaxSplit;
   smax = smax < 1 ? 1 : smax;
@@ -142,7 +144,7 @@ __host__ __device__ inline int stream_splits(int items, int KT) {
   s = s < smax ? s : smax;
   if (s + 1 <= smax) {
     const int u0 = items * s, u1 = items * (s + 1);
-    const int r0 = (u0 + kStreamSlots - 1) / kStreamSlots, r1b = (u1 + kStreamSlots - 1) / kStreamSlots;
+    const int r0 = (u0 + slots - 1) / slots, r1b = (u1 + slots - 1) / slots;
     // fill(s) = u / (rounds * slots); take s + 1 if it fills at least 5 points better
     if ((int64_t)u1 * r0 * 100 >= (int64_t)u0 * r1b * 105) s = s + 1;
   }
