@@ -25,7 +25,7 @@
 //
 // Pipeline: an LDS ring of 32 KB (bf16: 16 KB weights + 16 KB tokens, 5
 // stages) or 24 KB (fp8, 6 stages) stages filled with global_load_lds_dwordx4
-// several K steps ahead (bf16, fp4: issued after the step's last MFMA); one
+// several K steps ahead (issued late in the step, see kDmaAt); one
 // barrier per step; the fragments of step s+1 are read from LDS while the
 // MFMAs of step s run.  Token rows are read through the expert permutation
 // when a gather index is given; token tiles past the expert's last row skip
@@ -370,7 +370,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     if (full_loads) wait_steps<kLoads>(ahead);
     else wait_steps<kLoads - 1>(ahead);
   };
-  constexpr bool kDmaLate = kW != kWFp8;
+  // where a step's DMA is issued: 0 right after the barrier, 1 after the
+  // first MFMA half, 2 after the second, 3 after the step's LDS reads
+  // (measured per format and projection, dsv3 shapes: fp8 gate/up at 3 4.57
+  // ms against 4.85 at 0 and 5.15 at 1, fp8 down best at 0; fp4 at 2 3.73 ms
+  // against 3.92 at 1 and 4.08 at 3)
+  constexpr int kDmaAt = kW == kWFp8 ? (kMode == 0 ? 3 : 0) : 2;
+  constexpr bool kDmaLate = kDmaAt != 0;
   auto mainloop = [&](auto nt_const) {
     constexpr int NT = decltype(nt_const)::value;
     constexpr std::integral_constant<int, 0> h0{};
@@ -387,13 +393,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     wait_lgkm<0>();
     // One K step: the MFMAs of step s, with the fragments of step s+1 read
     // from LDS stage `next` half by half as the MFMAs free their registers.
-    // bf16 and fp4 issue the DMA of step fkt into stage fst (fkt < 0: none)
-    // after the last MFMA of the step: issued right after the barrier it
-    // delayed the MFMAs (gate/up: dsv3_bf16 4.85 -> 4.77 ms, expert-parallel
-    // shard 3.56 -> 3.43 ms, dsv3_fp4 3.98 -> 3.72 ms; issued between the two
-    // halves it was slower still).  fp8 (six stages, one MFMA per fragment
-    // half) keeps it right after the barrier: late, its gate/up took 5.12
-    // instead of 4.86 ms.
+    // The DMA of step fkt into stage fst (fkt < 0: none) is issued at
+    // position kDmaAt of the step.  Right after the barrier it delays the
+    // MFMAs: bf16 and fp4 issue it after the last MFMA (gate/up: dsv3_bf16
+    // 4.85 -> 4.77 ms, expert-parallel shard 3.56 -> 3.43 ms, dsv3_fp4 3.98
+    // -> 3.72 ms), fp8 gate/up after the step's LDS reads.
     auto body = [&](int s, int next, int fst, int fkt) {
       __builtin_amdgcn_sched_barrier(0);
       // this step's first half landed (fp4: and the scales, read before the
@@ -401,14 +405,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
       wait_lgkm<kFp4 ? 2 + 2 * NT : (kFp8 ? 0 : 2 + NT)>();
       mfma_half(f, h0, nt_const);
       __builtin_amdgcn_sched_barrier(0);
+      if (kDmaAt == 1 && fkt >= 0) issue(fst, fkt);
+      __builtin_amdgcn_sched_barrier(0);
       read_half(next, f, h0, nt_const);
       __builtin_amdgcn_sched_barrier(0);
       wait_lgkm<kFp4 ? 2 + 2 * NT : (kFp8 ? (NT >= 1 ? 2 : 0) : 2 + NT)>();   // ... and its second half
       mfma_half(f, h1, nt_const);
       __builtin_amdgcn_sched_barrier(0);
-      if (fkt >= 0) issue(fst, fkt);
+      if (kDmaAt == 2 && fkt >= 0) issue(fst, fkt);
       __builtin_amdgcn_sched_barrier(0);
       read_half(next, f, h1, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kDmaAt == 3 && fkt >= 0) issue(fst, fkt);
       __builtin_amdgcn_sched_barrier(0);
       promote(s, nt_const);
     };
