@@ -186,14 +186,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       const int next = stage + 1 == kStages ? 0 : stage + 1;
       wait_step(issued - 1 - (s + 1));   // step s+1 landed for this thread
       __builtin_amdgcn_s_barrier();      // ... and for every thread; step s-1's buffer is free
-      if (issued < KS) {
-        int stn = stage + kStages - 1;
-        stn = stn >= kStages ? stn - kStages : stn;
-        issue_stage(stn, issued * 32);
-        ++issued;
-      }
+      // the DMA of step `issued` into the stage of step s-1 goes out after
+      // the step's last MFMAs (right after the barrier it delayed them:
+      // qwen_prefill row-major gate/up 345 -> 335 us)
+      const bool do_issue = issued < KS;
+      int stn = stage + kStages - 1;
+      stn = stn >= kStages ? stn - kStages : stn;
+      const int k_issue = issued * 32;
+      issued += do_issue ? 1 : 0;
       read_frags(next, 0, a0, b0);
       mfmas(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_issue) issue_stage(stn, k_issue);
+      __builtin_amdgcn_sched_barrier(0);
       stage = next;
     }
     read_frags(stage, 1, a1, b1);   // last step
