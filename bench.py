@@ -273,7 +273,7 @@ def bench_backward(args, s, L, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
