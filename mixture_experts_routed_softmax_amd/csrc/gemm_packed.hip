@@ -371,11 +371,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     else wait_steps<kLoads - 1>(ahead);
   };
   // where a step's DMA is issued: 0 right after the barrier, 1 after the
-  // first MFMA half, 2 after the second, 3 after the step's LDS reads
-  // (measured per format and projection, dsv3 shapes: fp8 gate/up at 3 4.57
-  // ms against 4.85 at 0 and 5.15 at 1, fp8 down best at 0; fp4 at 2 3.73 ms
-  // against 3.92 at 1 and 4.08 at 3)
-  constexpr int kDmaAt = kW == kWFp8 ? (kMode == 0 ? 3 : 0) : 2;
+  // first MFMA half, 2 after the second, 3 after the step's LDS reads, 4
+  // after the fp8 block promotion (measured per format, dsv3 shapes: fp8
+  // gate/up 4.20 ms at 4, 4.57 at 3, 4.85 at 0, 5.15 at 1; fp8 down 2.23 ms
+  // at 4, 2.38 at 0; fp4 gate/up 3.73 ms at 2, 3.92 at 1, 4.08 at 3)
+  constexpr int kDmaAt = kW == kWFp8 ? 4 : 2;
   constexpr bool kDmaLate = kDmaAt != 0;
   auto mainloop = [&](auto nt_const) {
     constexpr int NT = decltype(nt_const)::value;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     // position kDmaAt of the step.  Right after the barrier it delays the
     // MFMAs: bf16 and fp4 issue it after the last MFMA (gate/up: dsv3_bf16
     // 4.85 -> 4.77 ms, expert-parallel shard 3.56 -> 3.43 ms, dsv3_fp4 3.98
-    // -> 3.72 ms), fp8 gate/up after the step's LDS reads.
+    // -> 3.72 ms), fp8 after the block promotion that ends the step.
     auto body = [&](int s, int next, int fst, int fkt) {
       __builtin_amdgcn_sched_barrier(0);
       // this step's first half landed (fp4: and the scales, read before the
@@ -419,6 +419,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
       if (kDmaAt == 3 && fkt >= 0) issue(fst, fkt);
       __builtin_amdgcn_sched_barrier(0);
       promote(s, nt_const);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kDmaAt == 4 && fkt >= 0) issue(fst, fkt);
     };
     int stage = 0;                  // LDS stage of step s
     int fill = kStages - 1;         // stage that receives step s + kStages - 1
