@@ -1,28 +1,36 @@
 """Throughput of the routed mixture-of-experts layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T N]
-                    [--scale-fmt f32|ue8m0] [--no-cpu-baseline] [--backward]
+                    [--scale-fmt f32|ue8m0] [--no-cpu-baseline] [--no-decode-extra]
+                    [--decode-steps N] [--backward]
 
 A step is one moe_forward call (router, permutation, gate/up + SwiGLU, down,
 combine) over one batch of T synthetic tokens whose inputs and weights are
 already resident in HBM.  W untimed warmup steps are followed by exactly K
-timed steps, bracketed by torch.cuda.synchronize(); value = T * K / elapsed.
+timed steps (default 20), bracketed by torch.cuda.synchronize();
+value = T / (elapsed / K).
 
 Expert weights are packed into the tile-contiguous layout once before the
 timed steps (moe_pack_weights, a model-load transform; --layout rowmajor
 times the unpacked kernels instead).
 
-The default workload is the Qwen1.5-MoE-A2.7B-like prefill layer (T=4096,
-H=2048, I=1408, E=60, top-4 softmax without renormalisation, Zipf-skewed
-router bias, bf16).  Other workloads (--config) print the same line for
-measurement.  The JSON line also carries:
+The default workload is the largest prefill layer, the DeepSeek-V3-like one
+(T=8192, H=7168, I=2048, E=256, top-8 sigmoid renormalised x 2.5,
+Zipf-skewed router bias, bf16, 22.5 GB of expert weights).  Other workloads
+(--config) print the same line.  The JSON line also carries:
 
 * roofline: the gate/up grouped GEMM (two thirds of the layer's FLOPs) for
   prefill workloads, priced at its algorithmic FLOPs 2*P*H*2I against the dense
-  MFMA peak of its dtype; for decode workloads (T <= 64) the whole layer's
-  touched-expert weight bytes against 8 TB/s.  Kernel durations come from HIP
-  events the library records around each of its launches on the caller's
-  stream during the timed steps.
+  MFMA peak of its dtype, plus the whole layer's fraction (layer_frac: expert
+  FLOPs 6*P*H*I over the step time); for decode workloads (T <= 64) the whole
+  step's touched-expert weight bytes against 8 TB/s.  Kernel durations come
+  from HIP events the library records around each of its launches on the
+  caller's stream during the timed steps.
+* decode (prefill lines): the Qwen-like decode layer at T=1 and T=64, each
+  the median of --decode-steps (default 200) individually timed steps with the
+  last-level cache evicted before each, as the fraction of 8 TB/s that the
+  touched experts' weight bytes give.  A decode workload's own line
+  (--config qwen_decode) is timed the same way.
 * cpu_baseline: the fp64 oracle (never tuned) on the host cores, on a bounded
   sample: the router over all T tokens plus the expert MLPs and the combine on
   a sample of tokens sized to about 10 s; tokens/s = 1 / (router time per
@@ -53,9 +61,14 @@ METRIC = "MoE-layer tokens/s; % MFMA peak (prefill), % HBM BW (decode)"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 20; decode workloads: --decode-steps)")
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="qwen_prefill",
+    p.add_argument("--decode-steps", type=int, default=200,
+                   help="individually timed steps of a decode measurement (median reported)")
+    p.add_argument("--no-decode-extra", dest="decode_extra", action="store_false",
+                   help="prefill workloads: skip the Qwen-like decode measurements at T=1 and T=64")
+    p.add_argument("--config", default="dsv3_bf16",
                    choices=["tiny", "qwen_prefill", "qwen_decode", "dsv3_bf16", "dsv3_fp8", "dsv3_fp4",
                             "dsv3_ep8_shard"])
     p.add_argument("--T", type=int, default=None)
@@ -102,12 +115,12 @@ def recorded_traffic(workload: str, kernel: str):
     return None
 
 
-def cpu_baseline(s, L, budget_s: float):
-    """Time the fp64 oracle on a bounded sample of this workload."""
+def cpu_baseline(s, hl, budget_s: float):
+    """Time the fp64 oracle on a bounded sample of this workload (hl: the
+    layer's tensors in host memory)."""
     import numpy as np
     import oracle
 
-    hl = {k: (None if v is None else v.detach().cpu()) for k, v in L.items()}
     score = oracle.SOFTMAX if s.score == "softmax" else oracle.SIGMOID
     gate = {"silu": oracle.GATE_SILU, "gelu": oracle.GATE_GELU, "relu": oracle.GATE_RELU}[s.gate]
     t0 = time.perf_counter()
@@ -270,44 +283,17 @@ def bench_backward(args, s, L, dev):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def run_layer(args, s, L, dev, steps: int, warmup: int, decode: bool):
+    """Times moe_forward on the resident layer L; returns the measurement.
 
+    Prefill (decode=False): `steps` back-to-back steps between two
+    synchronisations, with the library's per-launch stage events on (they
+    give the gate/up kernel's duration).  Decode: `steps` individually timed
+    steps (one event pair each, on the launch stream), each preceded by an
+    untimed read of a 2 GiB buffer that evicts the last-level cache; the
+    median step counts.  Packed weights are written once before timing."""
     import torch
     import mixture_experts_routed_softmax_amd as moe
-    import synthetic
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_calibration:
-        # a plain copy kernel of known size: it reads and writes exactly 1 GiB
-        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 copies of %d bytes" % src.numel())
-        return
-    over = {}
-    if args.T is not None:
-        over["T"] = args.T
-    if args.config == "dsv3_fp8":
-        over["scale_fmt"] = args.scale_fmt
-    if args.gate != "silu":
-        over["gate"] = args.gate
-    s = synthetic.spec(args.config, **over)
-    log("workload %s T=%d H=%d I=%d E=%d k=%d experts=%s" % (s.name, s.T, s.H, s.I, s.E, s.k, s.experts))
-    t0 = time.perf_counter()
-    L = synthetic.make_layer(s, seed=args.seed, device=dev)
-    torch.cuda.synchronize()
-    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
-    if args.backward:
-        bench_backward(args, s, L, dev)
-        return
 
     layout = args.layout if s.experts != "f32" else "rowmajor"
     d = moe.make_desc(s.T, s.H, s.I, s.E, s.k, score=s.score, renormalize=s.renormalize,
@@ -331,10 +317,9 @@ def main():
         moe.moe_forward(d, L["x"], L["w_router"], L["router_bias"], wg, wu, dn, L.get("s_gate"),
                         L.get("s_up"), L.get("s_down"), out, None, None, counts, ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    decode = s.T <= 64
     run = step
     graph = None
     if decode and args.graph != "off":
@@ -361,65 +346,129 @@ def main():
             else:
                 flush_buf.zero_()
         flush = flush_cache
-    # Prefill: the library records HIP events around each of its launches
-    # during the timed steps (the gate/up kernel's duration feeds the roofline).
-    # Decode: the roofline is the whole step, timed with one event pair per
-    # step; per-launch events would add their own cost to a ~0.1 ms step, so the
-    # per-stage breakdown comes from extra steps after the timed region.
+    # Decode steps are timed with one event pair per step; per-launch events
+    # would add their own cost to a ~0.1 ms step, so the per-stage breakdown
+    # comes from extra steps after the timed region.
     moe.moe_timing_enable(not decode)
     moe.moe_timing_read()
     if decode:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+              for _ in range(steps)]
         torch.cuda.synchronize()
-        for i in range(args.steps):
+        for i in range(steps):
             flush()
             ev[i][0].record(stream)
             run()
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         times = sorted(a.elapsed_time(b) for a, b in ev)
-        elapsed_ms = sum(times)
         ms_per_step = times[len(times) // 2]
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             step()
         torch.cuda.synchronize()
-        elapsed_ms = (time.perf_counter() - t0) * 1e3
-        ms_per_step = elapsed_ms / args.steps
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
     stages = moe.moe_timing_read()
     moe.moe_timing_enable(False)
     if decode:
         moe.moe_timing_enable(True)
         moe.moe_timing_read()
-        for _ in range(min(args.steps, 20)):
+        for _ in range(min(steps, 20)):
             flush()
             step()
         torch.cuda.synchronize()
         stages = moe.moe_timing_read()
         moe.moe_timing_enable(False)
+    cnt = counts.cpu()
+    del ws, wg, wu, dn, out
+    return {"ms_per_step": ms_per_step, "stages": stages, "counts": cnt, "layout": layout,
+            "graph": graph is not None, "launches": sum(n for _, n in stages.values()) / min(steps, 20)
+            if decode else None}
+
+
+def weight_bytes_per_expert(s) -> float:
+    b = 3 * s.H * s.I * {"fp4": 0.5, "fp8": 1, "bf16": 2, "f32": 4}[s.experts]
+    if s.experts == "fp4":
+        b += 3 * s.H * s.I // 32    # one UE8M0 scale byte per 32 weights
+    return b
+
+
+def decode_record(s, m, steps: int) -> dict:
+    """HBM roofline of a whole decode step: the touched experts' weight bytes
+    (each read once) over the median step time."""
+    touched = int((m["counts"] > 0).sum())
+    alg = touched * weight_bytes_per_expert(s)
+    gbs = alg / (m["ms_per_step"] / 1e3) / 1e9
+    return {"workload": s.name, "T": s.T, "ms_per_step": round(m["ms_per_step"], 4),
+            "tokens_per_s": round(s.T / (m["ms_per_step"] / 1e3), 1), "achieved_GBs": round(gbs, 1),
+            "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "touched_experts": touched,
+            "alg_bytes": alg, "steps": steps, "timing": "median of %d individually timed steps, last-level "
+            "cache evicted before each" % steps, "launches_per_step": m["launches"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a plain copy kernel of known size: it reads and writes exactly 1 GiB
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of %d bytes" % src.numel())
+        return
+    over = {}
+    if args.T is not None:
+        over["T"] = args.T
+    if args.config == "dsv3_fp8":
+        over["scale_fmt"] = args.scale_fmt
+    if args.gate != "silu":
+        over["gate"] = args.gate
+    s = synthetic.spec(args.config, **over)
+    decode = s.T <= 64
+    steps = args.steps if args.steps is not None else (args.decode_steps if decode else 20)
+    log("workload %s T=%d H=%d I=%d E=%d k=%d experts=%s" % (s.name, s.T, s.H, s.I, s.E, s.k, s.experts))
+    t0 = time.perf_counter()
+    L = synthetic.make_layer(s, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+    if args.backward:
+        args.steps = steps
+        bench_backward(args, s, L, dev)
+        return
+
+    m = run_layer(args, s, L, dev, steps, args.warmup, decode)
+    del L
+    torch.cuda.empty_cache()
+    ms_per_step, stages, cnt, layout = m["ms_per_step"], m["stages"], m["counts"], m["layout"]
     value = s.T / (ms_per_step / 1e3)
     for name, (ms, n) in stages.items():
         if n:
             log("  stage %-8s %8.1f us/launch  (%d launches)" % (name, 1e3 * ms / n, n))
 
     P = s.T * s.k
-    cnt = counts.cpu()
     touched = int((cnt > 0).sum())
-    wbytes_per_expert = 3 * s.H * s.I * {"fp4": 0.5, "fp8": 1, "bf16": 2, "f32": 4}[s.experts]
-    if s.experts == "fp4":
-        wbytes_per_expert += 3 * s.H * s.I // 32    # one UE8M0 scale byte per 32 weights
+    layer_flops = 2.0 * P * 3 * s.H * s.I
+    layer_tflops = layer_flops / (ms_per_step / 1e3) / 1e12
     if decode:
-        # HBM roofline of the whole step: weights of the touched experts only
-        alg_bytes = touched * wbytes_per_expert
-        achieved = alg_bytes / (ms_per_step / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+        rec = decode_record(s, m, steps)
+        roof = {"bound": "hbm", "achieved": rec["achieved_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": rec["frac"], "traffic": None,
                 "kernel": "moe_forward (whole step%s, median of %d individually timed steps)"
-                          % (", replayed as a HIP graph" if graph is not None else "", args.steps),
-                "alg_bytes_per_launch": alg_bytes, "touched_experts": touched}
+                          % (", replayed as a HIP graph" if m["graph"] else "", steps),
+                "alg_bytes_per_launch": rec["alg_bytes"], "touched_experts": touched}
     else:
         ms_gu, n_gu = stages["gate_up"]
         avg_ms = ms_gu / max(n_gu, 1)
@@ -432,23 +481,43 @@ def main():
                 "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "kernel": "gate_up grouped GEMM (%s)" % s.experts,
-                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": flops}
-    layer_flops = 2.0 * P * 3 * s.H * s.I
+                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": flops,
+                "layer_tflops": round(layer_tflops, 1), "layer_frac": round(layer_tflops / peak, 4)}
     log("layer: %.3f ms/step, %.0f tokens/s, %.1f TFLOP/s expert GEMMs, touched %d/%d experts, "
         "max/mean tokens per expert %d/%.1f"
-        % (ms_per_step, value, layer_flops / (ms_per_step / 1e3) / 1e12, touched, s.E, int(cnt.max()),
-           P / s.E))
+        % (ms_per_step, value, layer_tflops, touched, s.E, int(cnt.max()), P / s.E))
+
+    # the decode regime next to a prefill line: the Qwen-like decode layer at
+    # 1 and 64 tokens, HBM fraction of the whole step
+    dec = None
+    if not decode and args.decode_extra:
+        dec = []
+        for T in (1, 64):
+            sd = synthetic.spec("qwen_decode", T=T)
+            Ld = synthetic.make_layer(sd, seed=args.seed + T, device=dev)
+            md = run_layer(args, sd, Ld, dev, args.decode_steps, max(args.warmup, 3), True)
+            del Ld
+            torch.cuda.empty_cache()
+            r = decode_record(sd, md, args.decode_steps)
+            log("decode %s T=%d: %.1f us/step, %.0f GB/s = %.1f%% of HBM (%d touched experts, %.1f launches)"
+                % (sd.name, T, 1e3 * r["ms_per_step"], r["achieved_GBs"], 100 * r["frac"], r["touched_experts"],
+                   r["launches_per_step"]))
+            dec.append(r)
 
     cpu = None
     if not args.no_cpu_baseline:
-        del ws, wg, wu, dn
+        t0 = time.perf_counter()
         L = synthetic.make_layer(s, seed=args.seed, device=dev)   # the same seeded inputs, row-major
-        cpu = cpu_baseline(s, L, args.cpu_seconds)
+        hl = {k: (None if v is None else v.detach().cpu()) for k, v in L.items()}
+        del L
+        torch.cuda.empty_cache()
+        log("host copy of the layer for the oracle: %.1f s" % (time.perf_counter() - t0))
+        cpu = cpu_baseline(s, hl, args.cpu_seconds)
         log("cpu baseline: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3", "fp4": "fp4_e2m1"}[s.experts],
         "data": "synthetic",
@@ -457,10 +526,12 @@ def main():
                    "routed_scale": s.routed_scale, "router_bias": s.bias, "weights": layout,
                    **({"scale_fmt": s.scale_fmt} if s.experts in ("fp8", "fp4") else {}),
                    **({"gate": s.gate} if s.gate != "silu" else {}),
-                   "layer_tflops": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1)},
+                   "layer_tflops": round(layer_tflops, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if dec is not None:
+        line["decode"] = dec
     print(json.dumps(line), flush=True)
 
 

@@ -6,8 +6,9 @@
  * a router selects k of E experts; the token's hidden state is projected
  * through each selected expert's parameters and the k results are summed with
  * the routing weights.  Each expert is a gated MLP (backend table, row
- * deepgemm_megamoe; section "SonicMoE"): an up projection with a silu-gated
- * twin (SwiGLU), then a down projection.  Tokens are first ordered by their
+ * deepgemm_megamoe; section "SonicMoE"): a gate and an up projection combined
+ * as act(gate) * up, with act = silu (SwiGLU, the default), gelu (GeGLU) or
+ * relu (ReGLU) as desc->gate_act selects, then a down projection.  Tokens are first ordered by their
  * selected expert so that all experts run as one grouped GEMM (backend table,
  * rows grouped_mm and deepgemm).
  *
@@ -151,7 +152,7 @@ typedef struct moe_desc {
 
 /* ------------------------------------------------------------------------ */
 
-/* Router (opening paragraph: "a router selects k experts").
+/* Router (opening paragraph: the router picks k of the E experts per token).
  *   x           [T,H] act_dtype
  *   w_router    [E,H] act_dtype
  *   router_bias [E] fp32, added to the logits before scoring, or NULL
@@ -170,8 +171,8 @@ moe_status moe_route_topk(const moe_desc* desc, const void* x, const void* w_rou
 /* Order (token, slot) pairs by expert (backend table, rows grouped_mm and
  * deepgemm: tokens are ordered / sorted by selected expert).
  *   topk_ids        [T,k] int32 in, values in [0,E) (a pair with an id outside
- *                   that range is left out of counts; its perm/inv entries are
- *                   then undefined)
+ *                   that range is left out of counts and perm, and gets
+ *                   inv = -1; moe_unpermute_combine skips such pairs)
  *   counts          [E] out: pairs per expert
  *   offsets         [E+1] out: exclusive prefix sum of counts
  *   perm            [P] out: perm[row] = t*k + i, rows of one expert in
@@ -187,9 +188,11 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_ids, const void
                        void* x_sorted, float* x_sorted_scales,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Gate/up grouped GEMM with the SwiGLU epilogue, all experts in one launch.
- * Row r of expert e (offsets[e] <= r < offsets[e+1]):
- *   h[r, j] = silu(g) * u,  g = x_sorted[r] . w_gate[e, j],  u = x_sorted[r] . w_up[e, j]
+/* Gate/up grouped GEMM with the gated-activation epilogue, all experts in one
+ * launch.  Row r of expert e (offsets[e] <= r < offsets[e+1]):
+ *   h[r, j] = act(g) * u,  g = x_sorted[r] . w_gate[e, j],  u = x_sorted[r] . w_up[e, j]
+ *   act = silu (SwiGLU), gelu (exact erf form, GeGLU) or relu (ReGLU) per
+ *   desc->gate_act
  *   x_sorted      [P,H] act_dtype, or e4m3 codes with x_scales [P,H/128] (FP8)
  *   offsets       [E+1] from moe_permute
  *   w_gate, w_up  [E,I,H]; with FP8 also w_gate_scales, w_up_scales
@@ -214,9 +217,10 @@ moe_status moe_expert_down(const moe_desc* desc, const void* h, const float* h_s
                            const void* w_down_scales, void* y_sorted,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted combine back to token order (opening paragraph: "aggregated with
- * routing weights"):
+/* Weighted combine back to token order (opening paragraph: the experts'
+ * results are summed with the routing weights):
  *   out[t, :] = sum_{i<k} topk_w[t, i] * y_sorted[inv[t*k + i], :]
+ * (pairs with inv outside [0, P) are skipped)
  * summed in fp32 in slot order, rounded once to act_dtype.  No atomics: the
  * result is bitwise reproducible. */
 moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_sorted,

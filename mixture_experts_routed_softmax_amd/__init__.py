@@ -1,6 +1,8 @@
 """Routed mixture-of-experts forward on AMD MI355X (gfx950): Python binding.
 
-This module only marshals arguments to libmoe.so, the HIP library whose C ABI
+This module only marshals arguments to libmoe.so (and checks, before each
+call, that every tensor is a contiguous GPU tensor of an accepted dtype and
+large enough for the shapes in the description), the HIP library whose C ABI
 is declared in include/moe.h.  Every step of the layer runs in libmoe's
 kernels; PyTorch provides device memory and the current HIP stream.  The
 functions carry the names of the C entry points and take torch tensors (or
@@ -142,6 +144,89 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# ---- argument checks (before the call: the library cannot see tensor metadata)
+
+def _dtypes():
+    import torch
+    f8 = [getattr(torch, n) for n in ("float8_e4m3fn", "float8_e8m0fnu") if hasattr(torch, n)]
+    return {
+        "f32": (torch.float32,), "bf16": (torch.bfloat16,), "i32": (torch.int32,),
+        "bytes": None,   # any dtype: a raw byte buffer
+        "codes": (torch.uint8, torch.int8, *f8),
+    }
+
+
+_ELT = {MOE_DT_F32: 4, MOE_DT_BF16: 2, MOE_DT_FP8_E4M3: 1, MOE_DT_FP4_E2M1: 1}
+_KIND = {MOE_DT_F32: "f32", MOE_DT_BF16: "bf16", MOE_DT_FP8_E4M3: "codes", MOE_DT_FP4_E2M1: "codes"}
+
+
+def _arg(t, name: str, kind: str, nbytes: int):
+    """Raise ValueError unless the device tensor t can hold nbytes of `kind`:
+    a contiguous GPU tensor of an accepted dtype and at least nbytes long.
+    None and raw integer addresses pass unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    ok = _dtypes()[kind]
+    if ok is not None and t.dtype not in ok:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, [str(d) for d in ok]))
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes, %d needed" % (name, have, nbytes))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _known(desc) -> bool:
+    """Whether desc's dtypes and sizes are ones the checks can size; anything
+    else is left to the library's own validation (which rejects it)."""
+    return (desc.act_dtype in _ELT and desc.w_dtype in _ELT and desc.y_dtype in _ELT and
+            desc.w_scale_fmt in (MOE_SCALE_NONE, MOE_SCALE_F32, MOE_SCALE_UE8M0) and
+            min(desc.T, desc.H, desc.I, desc.E, desc.k) >= 0)
+
+
+def _fp8(desc) -> bool:
+    return desc.w_dtype in (MOE_DT_FP8_E4M3, MOE_DT_FP4_E2M1)
+
+
+def _w_bytes(desc, rows: int, cols: int) -> int:
+    """Bytes of one row-major expert matrix stack [E, rows, cols] in desc's weight format."""
+    per = cols // 2 if desc.w_dtype == MOE_DT_FP4_E2M1 else cols * _ELT[desc.w_dtype]
+    return desc.E * rows * per
+
+
+def _scale_bytes(desc, rows: int, cols: int) -> int:
+    if desc.w_dtype == MOE_DT_FP4_E2M1:
+        return desc.E * rows * (cols // 32)
+    per = 1 if desc.w_scale_fmt == MOE_SCALE_UE8M0 else 4
+    return desc.E * ((rows + 127) // 128) * ((cols + 127) // 128) * per
+
+
+def _check_weights(desc, w_gate, w_up, w_down, sg, su, sd):
+    H, I = desc.H, desc.I
+    if desc.w_layout == MOE_LAYOUT_PACKED:
+        _arg(w_gate, "w_gate (packed gate/up)", "bytes", moe_packed_weight_bytes(desc, MOE_PACK_GATE_UP))
+        _arg(w_down, "w_down (packed)", "bytes", moe_packed_weight_bytes(desc, MOE_PACK_DOWN))
+    else:
+        kind = _KIND[desc.w_dtype]
+        _arg(w_gate, "w_gate", kind, _w_bytes(desc, I, H))
+        _arg(w_up, "w_up", kind, _w_bytes(desc, I, H))
+        _arg(w_down, "w_down", kind, _w_bytes(desc, H, I))
+    if _fp8(desc):
+        skind = "f32" if desc.w_scale_fmt == MOE_SCALE_F32 and desc.w_dtype == MOE_DT_FP8_E4M3 else "codes"
+        _arg(sg, "w_gate_scales", skind, _scale_bytes(desc, I, H))
+        _arg(su, "w_up_scales", skind, _scale_bytes(desc, I, H))
+        _arg(sd, "w_down_scales", skind, _scale_bytes(desc, H, I))
+
+
+def _check_router(desc, x, w_router, router_bias):
+    ea = _ELT[desc.act_dtype]
+    _arg(x, "x", _KIND[desc.act_dtype], desc.T * desc.H * ea)
+    _arg(w_router, "w_router", _KIND[desc.act_dtype], desc.E * desc.H * ea)
+    _arg(router_bias, "router_bias", "f32", desc.E * 4)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -184,6 +269,12 @@ def moe_packed_weight_bytes(desc: MoeDesc, which: int) -> int:
 
 
 def moe_pack_weights(desc, which, w0, w1, dst, stream=None):
+    if _known(desc):
+        kind = _KIND[desc.w_dtype]
+        rows, cols = (desc.I, desc.H) if which == MOE_PACK_GATE_UP else (desc.H, desc.I)
+        _arg(w0, "w0", kind, _w_bytes(desc, rows, cols))
+        _arg(w1, "w1", kind, _w_bytes(desc, rows, cols))
+        _arg(dst, "dst", "bytes", moe_packed_weight_bytes(desc, which))
     _check(_lib.moe_pack_weights(ctypes.byref(desc), int(which), _ptr(w0), _ptr(w1), _ptr(dst),
                                  _stream(stream)))
 
@@ -199,12 +290,28 @@ def pack_experts(desc, w_gate, w_up, w_down, device="cuda"):
 
 
 def moe_route_topk(desc, x, w_router, router_bias, topk_ids, topk_w, ws=None, stream=None):
+    if _known(desc):
+        _check_router(desc, x, w_router, router_bias)
+        _arg(topk_ids, "topk_ids", "i32", desc.T * desc.k * 4)
+        _arg(topk_w, "topk_w", "f32", desc.T * desc.k * 4)
     _check(_lib.moe_route_topk(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias),
                                _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_permute(desc, topk_ids, x, counts, offsets, perm, inv, x_sorted=None, x_sorted_scales=None,
                 ws=None, stream=None):
+    if _known(desc):
+        P = desc.T * desc.k
+        _arg(topk_ids, "topk_ids", "i32", P * 4)
+        for t, n, b in ((counts, "counts", desc.E), (offsets, "offsets", desc.E + 1), (perm, "perm", P),
+                        (inv, "inv", P)):
+            _arg(t, n, "i32", b * 4)
+        _arg(x, "x", _KIND[desc.act_dtype], desc.T * desc.H * _ELT[desc.act_dtype])
+        if _fp8(desc):
+            _arg(x_sorted, "x_sorted", "codes", P * desc.H)
+            _arg(x_sorted_scales, "x_sorted_scales", "f32", P * (desc.H // 128) * 4)
+        else:
+            _arg(x_sorted, "x_sorted", _KIND[desc.act_dtype], P * desc.H * _ELT[desc.act_dtype])
     _check(_lib.moe_permute(ctypes.byref(desc), _ptr(topk_ids), _ptr(x), _ptr(counts), _ptr(offsets),
                             _ptr(perm), _ptr(inv), _ptr(x_sorted), _ptr(x_sorted_scales), _ptr(ws),
                             _nbytes(ws), _stream(stream)))
@@ -212,6 +319,18 @@ def moe_permute(desc, topk_ids, x, counts, offsets, perm, inv, x_sorted=None, x_
 
 def moe_expert_gate_up_swiglu(desc, x_sorted, x_scales, offsets, w_gate, w_up, w_gate_scales,
                               w_up_scales, h, h_scales, ws=None, stream=None):
+    if _known(desc):
+        P = desc.T * desc.k
+        _check_weights(desc, w_gate, w_up, None, w_gate_scales, w_up_scales, None)
+        _arg(offsets, "offsets", "i32", (desc.E + 1) * 4)
+        if _fp8(desc):
+            _arg(x_sorted, "x_sorted", "codes", P * desc.H)
+            _arg(x_scales, "x_scales", "f32", P * (desc.H // 128) * 4)
+            _arg(h, "h", "codes", P * desc.I)
+            _arg(h_scales, "h_scales", "f32", P * (desc.I // 128) * 4)
+        else:
+            _arg(x_sorted, "x_sorted", _KIND[desc.act_dtype], P * desc.H * _ELT[desc.act_dtype])
+            _arg(h, "h", _KIND[desc.act_dtype], P * desc.I * _ELT[desc.act_dtype])
     _check(_lib.moe_expert_gate_up_swiglu(ctypes.byref(desc), _ptr(x_sorted), _ptr(x_scales),
                                           _ptr(offsets), _ptr(w_gate), _ptr(w_up),
                                           _ptr(w_gate_scales), _ptr(w_up_scales), _ptr(h),
@@ -219,12 +338,28 @@ def moe_expert_gate_up_swiglu(desc, x_sorted, x_scales, offsets, w_gate, w_up, w
 
 
 def moe_expert_down(desc, h, h_scales, offsets, w_down, w_down_scales, y_sorted, ws=None, stream=None):
+    if _known(desc):
+        P = desc.T * desc.k
+        _check_weights(desc, None, None, w_down, None, None, w_down_scales)
+        _arg(offsets, "offsets", "i32", (desc.E + 1) * 4)
+        if _fp8(desc):
+            _arg(h, "h", "codes", P * desc.I)
+            _arg(h_scales, "h_scales", "f32", P * (desc.I // 128) * 4)
+        else:
+            _arg(h, "h", _KIND[desc.act_dtype], P * desc.I * _ELT[desc.act_dtype])
+        _arg(y_sorted, "y_sorted", _KIND[desc.y_dtype], P * desc.H * _ELT[desc.y_dtype])
     _check(_lib.moe_expert_down(ctypes.byref(desc), _ptr(h), _ptr(h_scales), _ptr(offsets),
                                 _ptr(w_down), _ptr(w_down_scales), _ptr(y_sorted), _ptr(ws),
                                 _nbytes(ws), _stream(stream)))
 
 
 def moe_unpermute_combine(desc, y_sorted, inv, topk_w, out, stream=None):
+    if _known(desc):
+        P = desc.T * desc.k
+        _arg(y_sorted, "y_sorted", _KIND[desc.y_dtype], P * desc.H * _ELT[desc.y_dtype])
+        _arg(inv, "inv", "i32", P * 4)
+        _arg(topk_w, "topk_w", "f32", P * 4)
+        _arg(out, "out", _KIND[desc.act_dtype], desc.T * desc.H * _ELT[desc.act_dtype])
     _check(_lib.moe_unpermute_combine(ctypes.byref(desc), _ptr(y_sorted), _ptr(inv), _ptr(topk_w),
                                       _ptr(out), _stream(stream)))
 
@@ -232,6 +367,13 @@ def moe_unpermute_combine(desc, y_sorted, inv, topk_w, out, stream=None):
 def moe_forward(desc, x, w_router, router_bias, w_gate, w_up, w_down, w_gate_scales, w_up_scales,
                 w_down_scales, out, topk_ids_out=None, topk_w_out=None, counts_out=None, ws=None,
                 stream=None):
+    if _known(desc):
+        _check_router(desc, x, w_router, router_bias)
+        _check_weights(desc, w_gate, w_up, w_down, w_gate_scales, w_up_scales, w_down_scales)
+        _arg(out, "out", _KIND[desc.act_dtype], desc.T * desc.H * _ELT[desc.act_dtype])
+        _arg(topk_ids_out, "topk_ids_out", "i32", desc.T * desc.k * 4)
+        _arg(topk_w_out, "topk_w_out", "f32", desc.T * desc.k * 4)
+        _arg(counts_out, "counts_out", "i32", desc.E * 4)
     _check(_lib.moe_forward(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias),
                             _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
                             _ptr(w_up_scales), _ptr(w_down_scales), _ptr(out), _ptr(topk_ids_out),
@@ -241,6 +383,15 @@ def moe_forward(desc, x, w_router, router_bias, w_gate, w_up, w_down, w_gate_sca
 
 def moe_backward(desc, x, w_router, router_bias, w_gate, w_up, w_down, d_out, dx, dw_router, d_bias,
                  dw_gate, dw_up, dw_down, ws=None, stream=None):
+    if _known(desc):
+        _check_router(desc, x, w_router, router_bias)
+        _check_weights(desc, w_gate, w_up, w_down, None, None, None)
+        ea = _ELT[desc.act_dtype]
+        _arg(d_out, "d_out", _KIND[desc.act_dtype], desc.T * desc.H * ea)
+        _arg(dx, "dx", _KIND[desc.act_dtype], desc.T * desc.H * ea)
+        _arg(dw_router, "dw_router", _KIND[desc.act_dtype], desc.E * desc.H * ea)
+        _arg(d_bias, "d_bias", "f32", desc.E * 4)
+        _check_weights(desc, dw_gate, dw_up, dw_down, None, None, None)
     _check(_lib.moe_backward(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate),
                              _ptr(w_up), _ptr(w_down), _ptr(d_out), _ptr(dx), _ptr(dw_router), _ptr(d_bias),
                              _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws),

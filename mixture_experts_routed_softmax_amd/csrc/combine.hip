@@ -20,7 +20,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   __shared__ float s_w[kMaxTopK];
   const int64_t t = blockIdx.x;
   if (threadIdx.x < k) {
-    s_row[threadIdx.x] = inv[t * k + threadIdx.x];
+    // a pair without a row of y (inv outside [0, T*k): an out-of-range id)
+    // contributes nothing
+    const int64_t row = inv[t * k + threadIdx.x];
+    s_row[threadIdx.x] = row >= 0 && row < (int64_t)gridDim.x * k ? (int)row : -1;
     s_w[threadIdx.x] = w[t * k + threadIdx.x];
   }
   __syncthreads();
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       for (int u = 0; u < 8; ++u) {
         v0[u] = f32x4{};
         v1[u] = f32x4{};
-        if (i0 + u < k) {
+        if (i0 + u < k && s_row[i0 + u] >= 0) {
           const int64_t base = (int64_t)s_row[i0 + u] * H + c * 8;
           if (kYF32) {
             v0[u] = *(const f32x4*)((const float*)y + base);
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (i0 + u >= k) break;
+        if (s_row[i0 + u] < 0) continue;
         const float wi = s_w[i0 + u];
         if (kYF32) {
 #pragma unroll

@@ -60,6 +60,11 @@ __device__ __forceinline__ float gate_fn(float g, int act) {
   return silu(g);
 }
 
+// Router keys: a NaN key ranks as -inf, so it loses to every number and ties
+// with -inf (lowest expert index first); every top-k round then takes a valid
+// untaken expert.
+__device__ __forceinline__ float nan_to_neg_inf(float v) { return v != v ? -INFINITY : v; }
+
 // value of an E8M0 scale byte: 2^(b-127)
 __device__ __forceinline__ float e8m0_to_f32(uint8_t b) { return __builtin_ldexpf(1.0f, (int)b - 127); }
 

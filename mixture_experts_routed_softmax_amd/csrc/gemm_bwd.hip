@@ -20,8 +20,8 @@
 // pieces addressed by lanes 4j + i / 4 (j = 0..3), so lanes that address four
 // consecutive K rows at four consecutive 4-column pieces produce the
 // transposed 4 x 16 block.  Two such reads form the 8 K values a lane of
-// v_mfma_f32_32x32x16_bf16 needs.  The reads are inline assembly followed by
-// one explicit lgkmcnt wait per K half (see frag_mn).
+// v_mfma_f32_32x32x16_bf16 needs.  The reads of a K half are one inline
+// assembly block that ends with its own lgkmcnt wait (see frags_mn2).
 //
 // Tile 256 (M) x 256 (N), K step 32, 8 waves of 64 x 128 (2 x 4 MFMA tiles),
 // 4 LDS stages of 32 KB (one workgroup per CU).  MN-major stages hold 32 K
@@ -68,19 +68,65 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, co
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// MFMA fragment of columns m0 .. m0+31, K half h (16 rows) of an MN-major stage.
-// The two transposed reads (K rows r and r+4: 2048 bytes apart, same swizzle)
-// are issued by inline assembly: the compiler treats the ds_read_tr builtin as
-// possibly aliasing the LDS DMA in flight and would wait for all of it before
-// each read.  The caller waits (lgkmcnt) before any use of the result.
-__device__ __forceinline__ bf16x8 frag_mn(const uint8_t* st, int h, int m0, int lane) {
+// LDS address of a lane's part of the MFMA fragment of columns m0 .. m0+31,
+// K half h (16 rows) of an MN-major stage; the fragment is two transposed
+// reads, at this address and 2048 bytes on (K rows r and r+4, same swizzle).
+__device__ __forceinline__ uint32_t mn_addr(const uint8_t* st, int h, int m0, int lane) {
   const int G = lane >> 4, s = lane & 15;
   const int col = m0 + (G & 1) * 16 + 4 * (s & 3);
   const int r = h * 16 + (G >> 1) * 8 + (s >> 2);
-  const uint32_t a0 = (uint32_t)(uintptr_t)(lds_void)(st + mn_off(r, col));
-  v4s lo, hi;
-  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048" : "=&v"(lo), "=&v"(hi) : "v"(a0));
+  return (uint32_t)(uintptr_t)(lds_void)(st + mn_off(r, col));
+}
+
+__device__ __forceinline__ bf16x8 join(v4s lo, v4s hi) {
   return __builtin_bit_cast(bf16x8, v8s{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+}
+
+// The transposed reads are inline assembly (the ds_read_tr builtin makes the
+// compiler wait for every LDS DMA in flight before each read), and each block
+// waits for its own reads (lgkmcnt(0)) before it ends, so its outputs are
+// complete when the compiler first sees them: no register of a read in
+// flight is ever reused or copied.  The memory clobber keeps the block in
+// program order with the barrier and the DMA builtins.
+// Two fragments (addresses p0, p1).
+__device__ __forceinline__ void frags_mn2(uint32_t p0, uint32_t p1, bf16x8& f0, bf16x8& f1) {
+  v4s a, b, c, d;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(p0), "v"(p1)
+      : "memory");
+  f0 = join(a, b);
+  f1 = join(c, d);
+}
+
+// Six fragments (addresses p[0..5]).
+__device__ __forceinline__ void frags_mn6(const uint32_t (&p)[6], bf16x8 (&f)[6]) {
+  v4s r[12];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %13\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %17\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5])
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 6; ++i) f[i] = join(r[2 * i], r[2 * i + 1]);
 }
 
 // kRK: ragged K (weight gradients) or ragged rows (data gradients).  kRouter
@@ -213,23 +259,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a)
     if (s + kStagesB - 1 < KT) issue((s + kStagesB - 1) % kStagesB, s + kStagesB - 1);
     const uint8_t* st = smem + (s % kStagesB) * kStageB;
     if (my_mt > 0 && my_nt > 0) {
-      // K half 0's fragments, then half 1's reads in flight under half 0's MFMAs
+      // per K half: the fragments (read and waited for), then their MFMAs;
+      // the other wave of the SIMD keeps the matrix pipe busy meanwhile
       bf16x8 fa[2][2], fb[2][4];
       auto read_half = [&](int h) {
+        if constexpr (kRK) {
+          const uint32_t p[6] = {mn_addr(st, h, wm * 64, lane), mn_addr(st, h, wm * 64 + 32, lane),
+                                 mn_addr(st + kOpBytes, h, wn * 128, lane),
+                                 mn_addr(st + kOpBytes, h, wn * 128 + 32, lane),
+                                 mn_addr(st + kOpBytes, h, wn * 128 + 64, lane),
+                                 mn_addr(st + kOpBytes, h, wn * 128 + 96, lane)};
+          bf16x8 f[6];
+          frags_mn6(p, f);
+          fa[h][0] = f[0];
+          fa[h][1] = f[1];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) fa[h][t] = frag_mn(st, h, wm * 64 + t * 32, lane);
+          for (int j = 0; j < 4; ++j) fb[h][j] = f[2 + j];
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (kRK) fb[h][j] = frag_mn(st + kOpBytes, h, wn * 128 + j * 32, lane);
-          else fb[h][j] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 128 + j * 32 + l32, h * 2 + hl));
+          for (int j = 0; j < 4; ++j)
+            fb[h][j] = *(const bf16x8*)(st + kOpBytes + km_off(wn * 128 + j * 32 + l32, h * 2 + hl));
+          frags_mn2(mn_addr(st, h, wm * 64, lane), mn_addr(st, h, wm * 64 + 32, lane), fa[h][0], fa[h][1]);
         }
-      };
-      // the transposed reads of half h land before any MFMA reads its
-      // fragments: the wait names them as operands, so no use moves above it
-      auto wait_half = [&](int h) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(fa[h][0]), "+v"(fa[h][1]), "+v"(fb[h][0]), "+v"(fb[h][1]), "+v"(fb[h][2]),
-                       "+v"(fb[h][3]));
       };
       auto mfma_half = [&](int h) {
 #pragma unroll
@@ -239,12 +290,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a)
             if (j < my_nt && t < my_mt) acc[t][j] = mfma_bf16(fa[h][t], fb[h][j], acc[t][j]);
       };
       read_half(0);
-      wait_half(0);
-      read_half(1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_half(1);
+      read_half(1);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_half(1);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -355,7 +405,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     float z = 0.f;
     if (e < E)
       for (int sl = 0; sl < slices; ++sl) z += part[((int64_t)sl * T + t) * E + e];
-    key[q] = e < E ? z + (bias ? bias[e] : 0.f) : -INFINITY;
+    key[q] = e < E ? nan_to_neg_inf(z + (bias ? bias[e] : 0.f)) : -INFINITY;
     ds[q] = 0.f;
   }
   if (score == 0) {
@@ -436,8 +486,11 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
   if (c >= H) return;
   f32x4 acc = *(const f32x4*)(dxr + t * H + c);
   f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t P = (int64_t)gridDim.x * k;
   for (int i = 0; i < k; ++i) {
-    const f32x4 v = *(const f32x4*)(dxp + (int64_t)inv[t * k + i] * H + c);
+    const int64_t row = inv[t * k + i];
+    if (row < 0 || row >= P) continue;   // a pair without a row contributes nothing
+    const f32x4 v = *(const f32x4*)(dxp + row * H + c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) sum[q] += v[q];
   }

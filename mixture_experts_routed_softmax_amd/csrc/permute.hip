@@ -216,6 +216,8 @@ __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ co
     for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
     perm[row] = tid;
     inv[tid] = row;
+  } else if (tid < P) {
+    inv[tid] = -1;   // a pair with an out-of-range id has no row
   }
   if (touched != nullptr) {
     if (tid < E) s_tiles[tid] = (s_offsets[tid + 1] - s_offsets[tid]) > 0 ? 1 : 0;
@@ -311,6 +313,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
       for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
       perm[row] = (int32_t)p;
       inv[p] = row;
+    } else if (p < P) {
+      inv[p] = -1;   // a pair with an out-of-range id has no row
     }
     __syncthreads();
     for (int x = tid; x < E; x += 256) {

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void route_topk_f32_kernel(
     for (int q = 0; q < 4; ++q) {
       int e = lane + 64 * q;
       taken[q] = !(e < E);
-      key[q] = e < E ? s_key[tl][e] + (bias ? bias[e] : 0.f) : -INFINITY;
+      key[q] = e < E ? nan_to_neg_inf(s_key[tl][e] + (bias ? bias[e] : 0.f)) : -INFINITY;
     }
     select_topk(key, taken, lane, E, k, score, renorm, routed_scale, ids_out + tok * k, w_out + tok * k);
   }

@@ -73,7 +73,8 @@ __device__ __forceinline__ void select_topk(float (&key)[4], bool (&taken)[4], i
 // Keys of token `tok` for a wave (lane l: experts l, l+64, l+128, l+192):
 // the slices' partial logits part[slice][T][E] added in ascending slice
 // order (the loads of 8 slices are issued together so that their latencies
-// overlap), plus the bias; experts past E are taken already.
+// overlap), plus the bias; experts past E are taken already and NaN keys
+// rank as -inf.
 __device__ __forceinline__ void token_keys(const float* __restrict__ part, int slices, int64_t T, int64_t tok, int E,
                                            const float* __restrict__ bias, int lane, float (&key)[4],
                                            bool (&taken)[4]) {
@@ -96,7 +97,7 @@ __device__ __forceinline__ void token_keys(const float* __restrict__ part, int s
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     taken[q] = !(e < E);
-    key[q] = e < E ? z[q] + (bias ? bias[e] : 0.f) : -INFINITY;
+    key[q] = e < E ? nan_to_neg_inf(z[q] + (bias ? bias[e] : 0.f)) : -INFINITY;
   }
 }
 

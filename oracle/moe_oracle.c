@@ -25,7 +25,8 @@
  * no shapes and no block size):
  *   - score = softmax over all E experts, or a logistic sigmoid, of
  *     key[e] = x . W_r[e] + bias[e]; selection is on key itself, descending,
- *     ties to the lowest expert index; slots are in selection order;
+ *     ties to the lowest expert index; slots are in selection order; a NaN
+ *     key ranks as -inf (the page says nothing of non-finite inputs);
  *   - optional renormalisation of the k selected scores to sum 1, then a
  *     multiplicative routed scale;
  *   - stable order within an expert: ascending (token, slot);
@@ -208,6 +209,10 @@ void orc_route(int64_t T, int H, int E, int k,
             for (int h = 0; h < H; ++h)
                 z += decode_elem(x, xdt, t * H + h) * decode_elem(w_r, wdt, (int64_t)e * H + h);
             key[e] = z + (bias ? (double)bias[e] : 0.0);
+            /* a NaN key (a NaN among the token's or the router's values)
+             * ranks as -inf: below every number, tied with -inf, so the
+             * lowest untaken index wins among such keys */
+            if (isnan(key[e])) key[e] = -INFINITY;
             if (keys_out) keys_out[t * E + e] = key[e];
         }
         /* selection: k passes, each taking the largest remaining key; a strict

@@ -130,23 +130,28 @@ def _act_dtype(s: LayerSpec):
     return torch.float32 if s.act == "f32" else torch.bfloat16
 
 
-def make_layer(s: LayerSpec, seed: int = 0, device="cpu") -> dict:
+def make_layer(s: LayerSpec, seed: int = 0, device="cpu", snap: bool = True, experts: bool = True) -> dict:
     """All inputs of one layer call, generated on `device` with seeded generators.
 
     Keys: x [T,H], w_router [E,H], router_bias [E] fp32 or None, w_gate, w_up
     [E,I,H], w_down [E,H,I], and for fp8 s_gate, s_up [E,I/128,H/128], s_down
-    [E,H/128,I/128] (float32, or uint8 E8M0 bytes)."""
+    [E,H/128,I/128] (float32, or uint8 E8M0 bytes).
+
+    snap=False draws x, W_r and the bias from the same distributions without
+    snapping them to the grids that keep every partial sum of a logit exact in
+    fp32 (router outputs then depend on the summation order); experts=False
+    leaves out the expert weights."""
     device = torch.device(device)
     out = {}
-    out["x"] = make_tokens(s, seed, device)
+    out["x"] = make_tokens(s, seed, device, snap)
 
     g = _gen(device, seed, s.name, "w_router")
     if s.act == "f32":
         wr = torch.randn(s.E, s.H, generator=g, device=device) * math.sqrt(1.0 / 128.0)
-        wr = _snap(wr, 12, 2047)
+        wr = _snap(wr, 12, 2047) if snap else wr
     else:
         wr = torch.randn(s.E, s.H, generator=g, device=device) * 0.02
-        wr = _snap(wr, 11, 255)
+        wr = _snap(wr, 11, 255) if snap else wr
     out["w_router"] = wr.to(_act_dtype(s))
 
     if s.bias == "none":
@@ -157,9 +162,12 @@ def make_layer(s: LayerSpec, seed: int = 0, device="cpu") -> dict:
         g = _gen("cpu", seed, s.name, "zipf_rank")
         rank = torch.randperm(s.E, generator=g).to(torch.float64) + 1.0
         b = -1.1 * torch.log(rank)
-        out["router_bias"] = _snap(b, 15, 1 << 22).to(torch.float32).to(device)
+        out["router_bias"] = (_snap(b, 15, 1 << 22) if snap else b).to(torch.float32).to(device)
 
-    _check_router_exact(s, out["x"], out["w_router"], out["router_bias"])
+    if snap:
+        _check_router_exact(s, out["x"], out["w_router"], out["router_bias"])
+    if not experts:
+        return out
 
     if s.experts == "fp8":
         out.update(_fp8_experts(s, seed, device))
@@ -170,10 +178,10 @@ def make_layer(s: LayerSpec, seed: int = 0, device="cpu") -> dict:
     return out
 
 
-def make_tokens(s: LayerSpec, seed: int, device) -> torch.Tensor:
+def make_tokens(s: LayerSpec, seed: int, device, snap: bool = True) -> torch.Tensor:
     g = _gen(device, seed, s.name, "x", s.T)
     x = torch.randn(s.T, s.H, generator=g, device=device)
-    return _snap(x, 4, 127).to(_act_dtype(s))
+    return (_snap(x, 4, 127) if snap else x).to(_act_dtype(s))
 
 
 def _check_router_exact(s, x, wr, bias):

@@ -188,3 +188,27 @@ def test_backward_validation():
     assert moe.moe_workspace_bytes(empty, moe.MOE_OP_BACKWARD) == 0
     # no token: the parameter gradients must be given (they are zero-filled)
     assert _status_of(lambda d: moe.moe_backward(d, *([None] * 13), stream=0), empty) == moe.MOE_EINVAL
+
+
+def test_binding_checks_tensor_arguments():
+    """The binding rejects, before any library call, a tensor that is not
+    contiguous, has the wrong dtype, is too small for the description, or does
+    not live on the GPU (the C ABI only sees raw addresses)."""
+    import torch
+    d = moe.make_desc(8, 128, 128, 4, 2)
+    ok = dict(x=torch.zeros(8, 128, dtype=torch.bfloat16), w_router=torch.zeros(4, 128, dtype=torch.bfloat16))
+
+    def route(**over):
+        a = dict(ok, **over)
+        ids = torch.zeros(8, 2, dtype=torch.int32)
+        w = torch.zeros(8, 2, dtype=torch.float32)
+        moe.moe_route_topk(d, a["x"], a["w_router"], None, ids, w, stream=0)
+
+    with pytest.raises(ValueError, match="contiguous"):
+        route(x=torch.zeros(128, 8, dtype=torch.bfloat16).t())
+    with pytest.raises(ValueError, match="dtype"):
+        route(x=torch.zeros(8, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="bytes"):
+        route(x=torch.zeros(7, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        route()

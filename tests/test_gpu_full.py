@@ -1,10 +1,13 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times (moe_forward, default path, packed expert weights).
 
-Routing and the permutation are checked for all tokens, bit for bit, against
-the oracle.  The expert outputs are checked on a coverage sample the oracle
-computes row by row: the tokens owning the first and last row of every
-non-empty expert segment (the ragged tail tiles) plus seeded random tokens.
+Routing is checked for all tokens, bit for bit, against the oracle: the ids
+and per-expert counts moe_forward returns, and the offsets, perm and inv that
+moe_permute (the same histogram / scan / scatter launches the forward runs)
+builds from those ids.  The expert outputs are checked on a coverage sample
+the oracle computes row by row: the tokens owning the first and last row of
+every non-empty expert segment (the ragged tail tiles) plus seeded random
+tokens.
 """
 import gc
 
@@ -14,7 +17,8 @@ import torch
 
 import oracle
 import synthetic
-from moe_cases import (coverage_tokens, host, oracle_experts, oracle_route, row_rel_err,
+import mixture_experts_routed_softmax_amd as moe
+from moe_cases import (coverage_tokens, desc_for, host, oracle_experts, oracle_route, row_rel_err,
                        run_forward, tol_of)
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +38,21 @@ def _full_case(s, seed, n_random, limit, layout="packed"):
     np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=1e-5, atol=1e-7)
     counts_o, offsets_o, perm_o, inv_o = oracle.permute(ids_o, s.E)
     assert np.array_equal(counts.cpu().numpy(), counts_o)
+    # the permutation of the forward's own ids, bit for bit
+    P = s.T * s.k
+    d = desc_for(s, layout=layout)
+    pc = torch.empty(s.E, dtype=torch.int32, device="cuda")
+    po = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+    pp = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+    pi = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d, ids, None, pc, po, pp, pi, ws=moe.workspace(d, moe.MOE_OP_PERMUTE))
+    torch.cuda.synchronize()
+    assert np.array_equal(pc.cpu().numpy(), counts_o)
+    assert np.array_equal(po.cpu().numpy(), offsets_o)
+    assert np.array_equal(pp.cpu().numpy(), perm_o), "perm differs on %d of %d rows" % (
+        int((pp.cpu().numpy() != perm_o).sum()), P)
+    assert np.array_equal(pi.cpu().numpy(), inv_o)
+    del pc, po, pp, pi
     toks = coverage_tokens(perm_o, offsets_o, s.k, n_random, seed=seed, limit=limit)
     ex = oracle_experts(s, hl)
     ref = ex.combine(hl["x"], ids_o, w_o, toks)
@@ -54,14 +73,14 @@ def test_qwen_decode_full(T):
 
 
 def test_dsv3_bf16_full():
-    _full_case(synthetic.spec("dsv3_bf16"), seed=0, n_random=32, limit=160)
+    # every expert's first and last row (about 540 tokens) plus 32 random ones
+    _full_case(synthetic.spec("dsv3_bf16"), seed=0, n_random=32, limit=None)
 
 
 @pytest.mark.parametrize("T", synthetic.TOKEN_COUNTS["dsv3_fp8"])
 @pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
 def test_dsv3_fp8_full(T, fmt):
-    _full_case(synthetic.spec("dsv3_fp8", T=T, scale_fmt=fmt), seed=1, n_random=32,
-               limit=160 if T > 64 else 64)
+    _full_case(synthetic.spec("dsv3_fp8", T=T, scale_fmt=fmt), seed=1, n_random=32, limit=None)
 
 
 @pytest.mark.parametrize("T", [64, 8192])

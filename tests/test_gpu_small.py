@@ -403,3 +403,86 @@ def test_stage_timing_counts_every_launch():
         assert n == 3 and ms > 0, (name, ms, n)
     assert sum(ms for ms, _ in st.values()) <= start.elapsed_time(stop) * 1.001
     assert moe.moe_timing_read()["gate_up"][1] == 0
+
+
+# ------------------------------------------------------------------ non-finite and invalid input
+
+NAN_CASES = [
+    ("qwen_prefill", 12, "packed"),      # selection inside the permutation launch, weight streaming
+    ("qwen_prefill", 40, "packed"),      # separate selection launch, weight streaming
+    ("qwen_prefill", 300, "packed"),     # LDS-staged router, grouped GEMM
+    ("qwen_prefill", 300, "rowmajor"),
+    ("dsv3_fp8", 40, "packed"),
+    ("dsv3_fp8", 300, "packed"),
+]
+
+
+@pytest.mark.parametrize("name,T,layout", NAN_CASES)
+def test_nan_token(name, T, layout):
+    """A NaN in one token's hidden state makes all of its keys NaN; they rank
+    as -inf, so the token takes experts 0..k-1 (as in the oracle), its output
+    row is not finite and every other row still matches the oracle."""
+    over = dict(T=T, H=256, I=384, E=16, k=4)
+    s = synthetic.spec(name, **over)
+    L = synthetic.make_layer(s, seed=31, device="cuda")
+    t0 = T // 3
+    L["x"][t0, 5] = float("nan")
+    hl = host(L)
+    ids_o, w_o = oracle_route(s, hl)
+    assert list(ids_o[t0]) == list(range(s.k))
+    out, ids, w, counts = run_forward(s, L, layout=layout)
+    got_ids = ids.cpu().numpy()
+    assert ((got_ids >= 0) & (got_ids < s.E)).all()
+    assert np.array_equal(got_ids, ids_o)
+    assert int(counts.cpu().sum()) == T * s.k
+    o = out.cpu().float().numpy()
+    assert not np.isfinite(o[t0]).any()
+    rest = np.array([t for t in range(T) if t != t0])
+    ref = oracle_experts(s, hl).combine(hl["x"], ids_o, w_o, rest)
+    assert np.isfinite(o[rest]).all()
+    assert row_rel_err(o[rest], ref) <= tol_of(s)
+
+
+@pytest.mark.parametrize("T", [100, 1500])
+def test_permute_out_of_range_ids(T):
+    """Ids outside [0, E) (a caller's bad input to the staged calls) get no
+    row: counts, offsets and perm cover the valid pairs in the stable order,
+    inv is -1 for the others, and the combine skips them."""
+    s = synthetic.spec("qwen_prefill", T=T, H=128, I=128, E=12, k=2)
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, s.E, (T, s.k)).astype(np.int32)
+    bad = rng.random((T, s.k)) < 0.1
+    ids[bad] = rng.choice(np.array([-1, s.E, 1000, -77], dtype=np.int32), int(bad.sum()))
+    flat = ids.ravel()
+    valid = (flat >= 0) & (flat < s.E)
+    counts_ref = np.bincount(flat[valid], minlength=s.E)
+    offsets_ref = np.concatenate([[0], np.cumsum(counts_ref)])
+    perm_ref = np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")]
+    inv_ref = np.full(flat.size, -1)
+    inv_ref[perm_ref] = np.arange(perm_ref.size)
+    d = desc_for(s)
+    P = T * s.k
+    counts = torch.empty(s.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.full((P,), -9, dtype=torch.int32, device="cuda")
+    inv = torch.full((P,), -9, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d, torch.from_numpy(ids).cuda(), None, counts, offsets, perm, inv,
+                    ws=moe.workspace(d, moe.MOE_OP_PERMUTE))
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), counts_ref)
+    assert np.array_equal(offsets.cpu().numpy(), offsets_ref)
+    n = perm_ref.size
+    assert np.array_equal(perm.cpu().numpy()[:n], perm_ref)
+    assert np.array_equal(inv.cpu().numpy(), inv_ref)
+    # combine over the valid rows only
+    y = torch.randn(P, s.H, device="cuda").to(torch.bfloat16)
+    wt = torch.rand(T, s.k, device="cuda")
+    out = torch.empty(T, s.H, dtype=torch.bfloat16, device="cuda")
+    moe.moe_unpermute_combine(d, y, inv, wt, out)
+    torch.cuda.synchronize()
+    y64 = y.cpu().double().numpy()
+    w64 = wt.cpu().double().numpy().ravel()
+    ref = np.zeros((T, s.H))
+    for p in np.flatnonzero(valid):
+        ref[p // s.k] += w64[p] * y64[inv_ref[p]]
+    np.testing.assert_allclose(out.cpu().double().numpy(), ref, rtol=1e-2, atol=1e-2)

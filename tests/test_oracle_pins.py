@@ -220,6 +220,26 @@ def test_route_ties_lowest_index():
     assert np.array_equal(ids, np.tile(np.arange(4), (16, 1)))
 
 
+def test_route_nan_keys_rank_as_neg_inf():
+    # reading: a NaN key (from a NaN among the inputs) ranks as -inf, ties to
+    # the lowest index; checked against a brute-force lexsort of the keys with
+    # NaN replaced by -inf
+    x, w = _tiny_router(T=12, H=8, E=6, seed=9)
+    w[2, 3] = np.nan          # expert 2's key is NaN for every token
+    x[5, 1] = np.nan          # every key of token 5 is NaN
+    for score in (oracle.SOFTMAX, oracle.SIGMOID):
+        ids, wt, keys = oracle.route(x, w, None, 4, score, False, 1.0, want_keys=True)
+        ref = x.astype(np.float64) @ w.astype(np.float64).T
+        ref = np.where(np.isnan(ref), -np.inf, ref)
+        assert np.array_equal(keys, ref)
+        for t in range(12):
+            order = np.lexsort((np.arange(6), -ref[t]))
+            assert list(ids[t]) == list(order[:4]), (score, t)
+        assert list(ids[5]) == [0, 1, 2, 3]
+        assert 2 not in ids[np.arange(12) != 5]
+        assert np.isfinite(wt[np.arange(12) != 5]).all()
+
+
 def test_route_k_equals_E_softmax_sums_to_one():
     x, w = _tiny_router(T=20, H=8, E=5)
     ids, wt, keys = oracle.route(x, w, None, 5, oracle.SOFTMAX, False, 1.0, want_keys=True)
