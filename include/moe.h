@@ -241,6 +241,31 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory or hand over a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as moe_forward without
+ * ws / ws_bytes: the workspace is carved out of a static device array of
+ * MOE_STATIC_SCRATCH_BYTES bytes inside the library, one per device, held from
+ * the library's load until the process ends.  The call allocates nothing.
+ *   - Layers with moe_workspace_bytes(desc, MOE_OP_FORWARD) above
+ *     MOE_STATIC_SCRATCH_BYTES are rejected with MOE_EWORKSPACE (every
+ *     decode-sized batch of the Qwen- and DeepSeek-like layers, T <= 64,
+ *     and the Qwen-like prefill layer fit; the DeepSeek-like prefill layer
+ *     does not).
+ *   - The current device must be the stream's device (else MOE_EINVAL).
+ *   - Every call on one device shares that device's array, and each call
+ *     overwrites what the previous one left there: calls that can overlap on
+ *     one device (two host threads, or two streams not ordered by events)
+ *     race and must be serialised by the caller.
+ *   - No stage timing is recorded for it (moe_timing_*). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+moe_status moe_forward_static(const moe_desc* desc, const void* x, const void* w_router,
+                              const float* router_bias, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* w_gate_scales,
+                              const void* w_up_scales, const void* w_down_scales, void* out,
+                              int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                              void* stream);
+
 /* Backward of the whole layer ("Experts backends", section "SonicMoE": the
  * backend built for training gated-MLP experts).  Every gradient of the layer
  * for the output gradient d_out, with the top-k selection held fixed (it is

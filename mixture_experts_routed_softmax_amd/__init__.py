@@ -80,6 +80,7 @@ _sigs = {
                     ctypes.c_size_t, _vp],
     "moe_backward": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                      ctypes.c_size_t, _vp],
+    "moe_forward_static": [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
 }
 for _name, _args in _sigs.items():
     getattr(_lib, _name).argtypes = _args
@@ -379,6 +380,25 @@ def moe_forward(desc, x, w_router, router_bias, w_gate, w_up, w_down, w_gate_sca
                             _ptr(w_up_scales), _ptr(w_down_scales), _ptr(out), _ptr(topk_ids_out),
                             _ptr(topk_w_out), _ptr(counts_out), _ptr(ws), _nbytes(ws),
                             _stream(stream)))
+
+
+MOE_STATIC_SCRATCH_BYTES = 256 << 20
+
+
+def moe_forward_static(desc, x, w_router, router_bias, w_gate, w_up, w_down, w_gate_scales, w_up_scales,
+                       w_down_scales, out, topk_ids_out=None, topk_w_out=None, counts_out=None, stream=None):
+    """moe_forward on the library's static scratch (no workspace argument)."""
+    if _known(desc):
+        _check_router(desc, x, w_router, router_bias)
+        _check_weights(desc, w_gate, w_up, w_down, w_gate_scales, w_up_scales, w_down_scales)
+        _arg(out, "out", _KIND[desc.act_dtype], desc.T * desc.H * _ELT[desc.act_dtype])
+        _arg(topk_ids_out, "topk_ids_out", "i32", desc.T * desc.k * 4)
+        _arg(topk_w_out, "topk_w_out", "f32", desc.T * desc.k * 4)
+        _arg(counts_out, "counts_out", "i32", desc.E * 4)
+    _check(_lib.moe_forward_static(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                   _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_gate_scales),
+                                   _ptr(w_up_scales), _ptr(w_down_scales), _ptr(out), _ptr(topk_ids_out),
+                                   _ptr(topk_w_out), _ptr(counts_out), _stream(stream)))
 
 
 def moe_backward(desc, x, w_router, router_bias, w_gate, w_up, w_down, d_out, dx, dw_router, d_bias,

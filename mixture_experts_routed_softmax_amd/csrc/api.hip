@@ -6,6 +6,7 @@
 #include <cstring>
 #include <string>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "moe.h"
@@ -301,6 +302,9 @@ struct TimedLaunch {
   hipEvent_t start, stop;
 };
 bool g_timing = false;
+// set for the duration of a no-allocation call: no stage events are created
+// or recorded (creating an event may allocate)
+thread_local bool g_no_events = false;
 std::vector<TimedLaunch> g_pending;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -332,7 +336,7 @@ struct StageTimer {
   hipStream_t s;
   hipEvent_t a = nullptr, b = nullptr;
   StageTimer(int st, hipStream_t stream) : stage(st), s(stream) {
-    if (!g_timing) return;
+    if (!g_timing || g_no_events) return;
     const bool own_start = st == MOE_STAGE_GATE_UP || st == MOE_STAGE_BWD_WEIGHT;
     if (g_chain && g_chain_stream == s && !own_start) {
       a = g_chain;
@@ -343,7 +347,7 @@ struct StageTimer {
     b = pool_event();
   }
   ~StageTimer() {
-    if (!g_timing || !a || !b) return;
+    if (!g_timing || g_no_events || !a || !b) return;
     hipEventRecord(b, s);
     g_pending.push_back({stage, a, b});
     g_chain = b;
@@ -587,6 +591,48 @@ size_t backward_ws_size(const moe_desc* d) {
 
 }  // namespace
 
+// ---- static scratch of the no-allocation forward ---------------------------
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): moe_forward_static carves its workspace out of this
+// file-scope array instead of a caller buffer.  Each device holds its own copy
+// at its own address from module load until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is taken once per device with hipGetSymbolAddress (with that device
+// current) and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, which must be the
+// stream's device.
+moe_status static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  MOE_TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EINVAL, "device %d out of range", dev);
+  if (stream != nullptr) {
+    int sdev = -1;
+    MOE_TRY_HIP(hipStreamGetDevice(stream, &sdev), "hipStreamGetDevice");
+    if (sdev != dev) return fail(MOE_EINVAL, "the stream belongs to device %d, the current device is %d", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    MOE_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || ((uintptr_t)p & (kAlign - 1)) != 0) return fail(MOE_EHIP, "static scratch address unusable");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
 // ============================================================================
 extern "C" {
 
@@ -729,10 +775,12 @@ moe_status moe_unpermute_combine(const moe_desc* d, const void* y_sorted, const 
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* bias,
-                       const void* w_gate, const void* w_up, const void* w_down, const void* sg,
-                       const void* su, const void* sd, void* out, int32_t* ids_out, float* w_out,
-                       int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
+// The fused forward on a workspace of at least ws_size(d, MOE_OP_FORWARD)
+// bytes (moe_forward: the caller's; moe_forward_static: the static scratch).
+static moe_status forward_impl(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                        const void* w_gate, const void* w_up, const void* w_down, const void* sg,
+                        const void* su, const void* sd, void* out, int32_t* ids_out, float* w_out,
+                        int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   g_chain = nullptr;
   moe_status s = validate(d);
@@ -803,6 +851,37 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, c
                 "combine launch");
   }
   return MOE_OK;
+}
+
+moe_status moe_forward(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                       const void* w_gate, const void* w_up, const void* w_down, const void* sg,
+                       const void* su, const void* sd, void* out, int32_t* ids_out, float* w_out,
+                       int32_t* counts_out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(d, x, w_router, bias, w_gate, w_up, w_down, sg, su, sd, out, ids_out, w_out, counts_out, ws,
+                      ws_bytes, stream);
+}
+
+moe_status moe_forward_static(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                              const void* w_gate, const void* w_up, const void* w_down, const void* sg,
+                              const void* su, const void* sd, void* out, int32_t* ids_out, float* w_out,
+                              int32_t* counts_out, void* stream) {
+  g_err.clear();
+  g_chain = nullptr;
+  moe_status s = validate(d);
+  if (s != MOE_OK) return s;
+  const size_t need = ws_size(d, MOE_OP_FORWARD);
+  if (need > kStaticScratchBytes)
+    return fail(MOE_EWORKSPACE,
+                "moe_forward_static: this layer needs %zu bytes of scratch, more than the %zu bytes of the static "
+                "scratch (use moe_forward with a caller workspace)",
+                need, kStaticScratchBytes);
+  void* scratch_ptr = nullptr;
+  if ((s = static_scratch((hipStream_t)stream, &scratch_ptr)) != MOE_OK) return s;
+  g_no_events = true;
+  s = forward_impl(d, x, w_router, bias, w_gate, w_up, w_down, sg, su, sd, out, ids_out, w_out, counts_out,
+                   scratch_ptr, kStaticScratchBytes, stream);
+  g_no_events = false;
+  return s;
 }
 
 moe_status moe_backward(const moe_desc* d0, const void* x, const void* w_router, const float* bias,
