@@ -426,9 +426,12 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   StageTimer tm(MOE_STAGE_GATE_UP, st);
   hipError_t e;
   const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
+  const int64_t act_rows = gather ? d->T : pairs(d);   // x (read through perm) or x_sorted
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), d->T <= 32, st);
+  else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(act_rows, d->H))
+    e = launch_gemm_grouped_bf16(a, act_rows, 0, grid, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
@@ -458,6 +461,8 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), d->T <= 32, st);
+  else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(pairs(d), d->I))
+    e = launch_gemm_grouped_bf16(a, pairs(d), 1, grid, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);

@@ -92,6 +92,7 @@ struct GemmArgs {
   float* partial;           // weight streaming: split-K partial tiles
   int gate_act;             // moe_gate_act of the gate/up epilogue
   int gu_out;               // row-major bf16 gate/up: store g and u (fp32 [P, 2N]) instead of h
+  int64_t act_rows;         // rows of `act` (bounds of the activation buffer resource)
 };
 
 // tile geometry of the grouped GEMMs
@@ -109,6 +110,12 @@ hipError_t launch_gate_up_f32(const GemmArgs& a, hipStream_t stream);
 // grouped GEMM on tile-packed weights (bf16 or fp8), mode 0 gate/up, 1 down
 // wfmt: weight format, 0 bf16, 1 fp8, 2 fp4 (e4m3 activations for 1 and 2)
 hipError_t launch_gemm_packed(const GemmArgs& a, int wfmt, int mode, int grid, hipStream_t stream);
+// bf16 grouped GEMM on packed weights with one wave per SIMD (weights loaded
+// straight into registers, token rows through LDS); mode 0 gate/up, 1 down.
+// Takes K a multiple of 64 and activations of act_rows rows spanning at most
+// 4 GiB (32-bit row offsets); gemm_packed_kernel serves the rest.
+bool gemm_grouped_bf16_fits(int64_t act_rows, int K);
+hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
 constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
 // weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per
