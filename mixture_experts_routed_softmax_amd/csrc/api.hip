@@ -238,6 +238,7 @@ struct ForwardWs {
   float* hs;
   void* y;
   float* partial;
+  int32_t* rowinfo;   // weight streaming: where the down launch left each row
 };
 
 ForwardWs carve_forward(Carve& c, const moe_desc* d) {
@@ -259,7 +260,10 @@ ForwardWs carve_forward(Carve& c, const moe_desc* d) {
   w.h = c.take<uint8_t>((size_t)P * d->I * (is_fp8(d) ? 1 : elt_bytes(d->w_dtype)));
   if (is_fp8(d)) w.hs = c.take<float>((size_t)P * (d->I / 128));
   w.y = c.take<uint8_t>((size_t)P * d->H * elt_bytes(d->y_dtype));
-  if (use_stream(d)) w.partial = (float*)c.take<uint8_t>(stream_partial_bytes(d));
+  if (use_stream(d)) {
+    w.partial = (float*)c.take<uint8_t>(stream_partial_bytes(d));
+    w.rowinfo = c.take<int32_t>(P);
+  }
   return w;
 }
 
@@ -440,9 +444,13 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   return MOE_OK;
 }
 
+// rowinfo (weight streaming only): skip the split-K reduction launch and
+// leave a split launch's y in the partial tiles for launch_combine_stream
 moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int32_t* offsets,
-                    const void* wd, const void* sd, void* y, const Schedule* sched, float* partial, hipStream_t st) {
+                    const void* wd, const void* sd, void* y, const Schedule* sched, float* partial, hipStream_t st,
+                    int32_t* rowinfo = nullptr) {
   GemmArgs a = gemm_common(d);
+  a.rowinfo = rowinfo;
   a.partial = partial;
   a.act = h;
   a.act_scales = hs;
@@ -460,7 +468,8 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
-                           (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), d->T <= 32, st);
+                           (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), d->T <= 32, st,
+                           rowinfo == nullptr);
   else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(pairs(d), d->I))
     e = launch_gemm_grouped_bf16(a, pairs(d), 1, grid, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 1, grid, st);
@@ -848,6 +857,24 @@ static moe_status forward_impl(const moe_desc* d, const void* x, const void* w_r
   if ((s = run_gate_up(d, act, act_scales, fw.perm, fw.offsets, w_gate, w_up, sg, su, fw.h, fw.hs, fw.sched_gu, fw.partial,
                        st)) != MOE_OK)
     return s;
+  // Weight streaming: when even the most items the batch can touch leave the
+  // down launch unsplit (the usual case), its reduction launch is left out and
+  // the combine reads y, or sums the partial tiles should fewer experts make
+  // it split after all.  (With few items the reduction launch spreads the
+  // partial sums over many CUs, where a combine workgroup per token would not.)
+  const int64_t dn_items_max = std::min<int64_t>(d->E, P) * down_ntiles(d);
+  if (use_stream(d) && stream_splits((int)std::min<int64_t>(dn_items_max, 1 << 30), stream_ksteps(wfmt(d), d->I),
+                                     stream_slots(wfmt(d), d->T <= 32)) == 1) {
+    if ((s = run_down(d, fw.h, fw.hs, fw.offsets, w_down, sd, fw.y, fw.sched_dn, fw.partial, st, fw.rowinfo)) !=
+        MOE_OK)
+      return s;
+    StageTimer tm(MOE_STAGE_COMBINE, st);
+    MOE_TRY_HIP(launch_combine_stream(fw.y, d->y_dtype == MOE_DT_F32, fw.partial, fw.rowinfo, fw.sched_dn,
+                                      stream_ksteps(wfmt(d), d->I), stream_slots(wfmt(d), d->T <= 32), fw.inv, w,
+                                      d->T, d->k, d->H, out, d->act_dtype == MOE_DT_F32, st),
+                "combine launch");
+    return MOE_OK;
+  }
   if ((s = run_down(d, fw.h, fw.hs, fw.offsets, w_down, sd, fw.y, fw.sched_dn, fw.partial, st)) != MOE_OK) return s;
   {
     StageTimer tm(MOE_STAGE_COMBINE, st);

@@ -83,7 +83,121 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   }
 }
 
+// The combine after a streaming down launch without its reduction launch.
+// When that launch was split (S > 1, the same function of its item count as
+// the launch's), y row r of channel tile nt is the sum, in split order, of
+// the partial rows of the units (item, 0 .. S-1), item = rowinfo[r] / 64 + nt,
+// at row rowinfo[r] % 64 of each partial tile, rounded to y's type; else the
+// launch wrote y.  Then out[t, :] as in combine_kernel.
+template <bool kYF32, bool kOutF32>
+__global__ __launch_bounds__(256) void combine_split_kernel(const void* __restrict__ y,
+                                                            const float* __restrict__ partial,
+                                                            const int32_t* __restrict__ rowinfo,
+                                                            const Schedule* __restrict__ sched, int ksteps,
+                                                            int slots, const int32_t* __restrict__ inv,
+                                                            const float* __restrict__ w, int k, int H,
+                                                            void* __restrict__ out) {
+  __shared__ int s_row[kMaxTopK];
+  __shared__ int s_info[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
+  const int64_t t = blockIdx.x;
+  const int S = stream_splits(sched->total, ksteps, slots);
+  if (threadIdx.x < k) {
+    const int64_t row = inv[t * k + threadIdx.x];
+    const bool ok = row >= 0 && row < (int64_t)gridDim.x * k;
+    s_row[threadIdx.x] = ok ? (int)row : -1;
+    s_info[threadIdx.x] = ok && S > 1 ? rowinfo[row] : 0;
+    s_w[threadIdx.x] = w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int c = blockIdx.y * 256 + threadIdx.x;   // group of 8 channels
+  if (c >= H / 8) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int nt = c / 32, cc = (c % 32) * 8;   // channel tile, channel within it
+  for (int i = 0; i < k; ++i) {
+    if (s_row[i] < 0) continue;
+    float v[8];
+    if (S == 1) {
+      const int64_t base = (int64_t)s_row[i] * H + c * 8;
+      if (kYF32) {
+        const f32x4 v0 = *(const f32x4*)((const float*)y + base);
+        const f32x4 v1 = *(const f32x4*)((const float*)y + base + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = v0[q];
+          v[4 + q] = v1[q];
+        }
+      } else {
+        const i32x4 b = *(const i32x4*)((const uint16_t*)y + base);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = bf16_bits_to_f32((uint16_t)((uint32_t)b[q] & 0xffff));
+          v[2 * q + 1] = bf16_bits_to_f32((uint16_t)((uint32_t)b[q] >> 16));
+        }
+      }
+    } else {
+      const int info = s_info[i];
+      const int64_t u0 = (int64_t)(info / 64 + nt) * S;
+      const float* p0 = partial + u0 * kStreamPartFloats + (info % 64) * 256 + cc;
+      // the loads of all (at most kStreamMaxSplit) splits first, then the
+      // split-ordered sum
+      f32x4 a0[kStreamMaxSplit], a1[kStreamMaxSplit];
+#pragma unroll
+      for (int sp = 0; sp < kStreamMaxSplit; ++sp) {
+        const int64_t o = (int64_t)(sp < S ? sp : S - 1) * kStreamPartFloats;   // (unconditional loads)
+        a0[sp] = *(const f32x4*)(p0 + o);
+        a1[sp] = *(const f32x4*)(p0 + o + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < kStreamMaxSplit; ++sp) {
+        if (sp >= S) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] += a0[sp][q];
+          v[4 + q] += a1[sp][q];
+        }
+      }
+      if (!kYF32) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = bf16_bits_to_f32(f32_to_bf16_bits(v[q]));
+      }
+    }
+    const float wi = s_w[i];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wi, v[q], acc[q]);
+  }
+  const int64_t o = t * H + c * 8;
+  if (kOutF32) {
+    *(f32x4*)((float*)out + o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)((float*)out + o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    i32x4 pk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pk[q] = (int)pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *(i32x4*)((uint16_t*)out + o) = pk;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_stream(const void* y, int y_f32, const float* partial, const int32_t* rowinfo,
+                                 const Schedule* sched, int ksteps, int slots, const int32_t* inv, const float* w,
+                                 int64_t T, int k, int H, void* out, int out_f32, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (H % 8 != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)T, (unsigned)((H / 8 + 255) / 256)), block(256);
+#define MOE_COMBINE_SPLIT(YF, OF)                                                                        \
+  hipLaunchKernelGGL((combine_split_kernel<YF, OF>), grid, block, 0, stream, y, partial, rowinfo, sched, \
+                     ksteps, slots, inv, w, k, H, out)
+  if (y_f32 && out_f32) MOE_COMBINE_SPLIT(true, true);
+  else if (y_f32) MOE_COMBINE_SPLIT(true, false);
+  else if (out_f32) MOE_COMBINE_SPLIT(false, true);
+  else MOE_COMBINE_SPLIT(false, false);
+#undef MOE_COMBINE_SPLIT
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const float* w, int64_t T,
                           int k, int H, void* out, int out_f32, hipStream_t stream) {

@@ -401,6 +401,11 @@ __global__ __launch_bounds__(256, (kBlocksPerCu<kW, kOneTile>)) void gemm_stream
   if (u < 0) return;
   const int w = u / S, sp = u - w * S;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
+  // down without its reduction launch: where each sorted row's partial rows
+  // are (the items of an expert's channel tiles are consecutive)
+  if (kMode == 1 && a.rowinfo != nullptr && sp == 0 && it.ntile == 0 &&
+      (int)threadIdx.x < it.row_end - it.row_begin)
+    a.rowinfo[it.row_begin + threadIdx.x] = w * 64 + threadIdx.x;
   const int kt0 = (int)((int64_t)KT * sp / S), kt1 = (int)((int64_t)KT * (sp + 1) / S);
   float* part = S > 1 ? a.partial + (int64_t)u * kStreamPartFloats : nullptr;
   if (!kOneTile && it.row_end - it.row_begin > 32)
@@ -500,14 +505,26 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
 
 }  // namespace
 
+int stream_slots(int wfmt, int one_tile) {
+  if (wfmt == kWFp4) return one_tile ? kSlots<kWFp4, true> : kSlots<kWFp4, false>;
+  if (wfmt == kWFp8) return one_tile ? kSlots<kWFp8, true> : kSlots<kWFp8, false>;
+  return one_tile ? kSlots<kWBf16, true> : kSlots<kWBf16, false>;
+}
+
+int stream_ksteps(int wfmt, int K) {
+  return wfmt == kWFp4 ? stream_steps<kWFp4>(K) : (wfmt == kWFp8 ? stream_steps<kWFp8>(K) : stream_steps<kWBf16>(K));
+}
+
 hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, int one_tile,
-                              hipStream_t stream) {
+                              hipStream_t stream, int with_reduce) {
   if (grid == 0) return hipSuccess;
+  if (!with_reduce && (mode != 1 || a.rowinfo == nullptr)) return hipErrorInvalidValue;
   dim3 g(grid), rg(reduce_grid), b(256);
-#define MOE_STREAM_LAUNCH_T(W, M, F32, ONE)                                            \
-  do {                                                                                 \
-    hipLaunchKernelGGL((gemm_stream_kernel<W, M, F32, ONE>), g, b, 0, stream, a);      \
-    hipLaunchKernelGGL((stream_reduce_kernel<W, M, F32, ONE>), rg, b, 0, stream, a);   \
+#define MOE_STREAM_LAUNCH_T(W, M, F32, ONE)                                              \
+  do {                                                                                   \
+    hipLaunchKernelGGL((gemm_stream_kernel<W, M, F32, ONE>), g, b, 0, stream, a);        \
+    if (with_reduce)                                                                     \
+      hipLaunchKernelGGL((stream_reduce_kernel<W, M, F32, ONE>), rg, b, 0, stream, a);   \
   } while (0)
 #define MOE_STREAM_LAUNCH(W, M, F32)                      \
   do {                                                    \

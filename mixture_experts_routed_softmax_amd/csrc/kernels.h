@@ -93,6 +93,7 @@ struct GemmArgs {
   int gate_act;             // moe_gate_act of the gate/up epilogue
   int gu_out;               // row-major bf16 gate/up: store g and u (fp32 [P, 2N]) instead of h
   int64_t act_rows;         // rows of `act` (bounds of the activation buffer resource)
+  int32_t* rowinfo;         // streaming down without its reduction launch: sorted row -> item * 64 + row in item
 };
 
 // tile geometry of the grouped GEMMs
@@ -124,8 +125,13 @@ constexpr int kPackedDownChannels = 256;     // output channels per packed down 
 // fewer than kStreamTarget items are ever split)
 // wfmt: weight format, 0 bf16, 1 fp8, 2 fp4 (fp8 activations for 1 and 2)
 // one_tile: every expert holds at most 32 of the batch's rows (T <= 32)
+// with_reduce = 0 (down only): no reduction launch; a split launch leaves
+// y in the partial tiles (a.rowinfo says where) for launch_combine_stream
 hipError_t launch_gemm_stream(const GemmArgs& a, int wfmt, int mode, int grid, int reduce_grid, int one_tile,
-                              hipStream_t stream);
+                              hipStream_t stream, int with_reduce = 1);
+// workgroups resident at once and K steps of the streaming GEMM (they fix its splits)
+int stream_slots(int wfmt, int one_tile);
+int stream_ksteps(int wfmt, int K);
 constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamMaxScaleBlocks = 64;   // fp8 streaming: K / 128 at most (K <= 8192)
 constexpr int kStreamTarget = 1024;      // work units the split aims for (two rounds of 2 per CU)
@@ -221,5 +227,11 @@ hipError_t launch_chunk_sum(const float* part, int chunks, int64_t n, uint16_t* 
 // ---- combine
 hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const float* w, int64_t T,
                           int k, int H, void* out, int out_f32, hipStream_t stream);
+// after a streaming down launch without its reduction: y rows from y when the
+// launch was not split, else summed from its partial tiles (split order) and
+// rounded to y's type first; then the combine above, same arithmetic
+hipError_t launch_combine_stream(const void* y, int y_f32, const float* partial, const int32_t* rowinfo,
+                                 const Schedule* sched, int ksteps, int slots, const int32_t* inv, const float* w,
+                                 int64_t T, int k, int H, void* out, int out_f32, hipStream_t stream);
 
 }  // namespace moe

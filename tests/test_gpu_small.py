@@ -302,6 +302,29 @@ def test_stream_forward(name):
         assert int(counts.max()) > 32
 
 
+@pytest.mark.parametrize("y_dtype", [None, "f32"])
+def test_stream_combine_sums_down_partials(y_dtype):
+    """A decode batch whose down launch would be unsplit with as many
+    touched experts as it could have (512 items on 512 workgroups), so the
+    forward leaves out the down reduction launch; routing concentrated on 8
+    experts makes the launch split after all, and the combine sums the
+    partial tiles itself."""
+    s = synthetic.spec("dsv3_bf16", T=64, H=512, I=256, E=256, k=8)
+    L, hl = _layer(s, seed=21)
+    b = torch.zeros(s.E, dtype=torch.float32, device="cuda")
+    b[:8] = 64.0
+    L["router_bias"] = b
+    hl["router_bias"] = b.cpu()
+    ids_o, w_o = oracle_route(s, hl)
+    out, ids, w, counts = run_forward(s, L, path="stream", y_dtype=y_dtype, layout="packed")
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert int((counts > 0).sum()) == 8
+    out_o = oracle_experts(s, hl).combine(hl["x"], ids_o, w_o)
+    err = row_rel_err(out.cpu().float().numpy(), out_o)
+    print("concentrated stream (y %s): max row rel err %.3e" % (y_dtype, err))
+    assert err <= tol_of(s)
+
+
 @pytest.mark.parametrize("name", ["bf16_decode", "fp8_decode_f32"])
 def test_stream_staged_matches_oracle(name):
     s = STREAM[name]
