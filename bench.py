@@ -475,7 +475,12 @@ def main():
         flops = 2.0 * P * s.H * 2 * s.I
         achieved = flops / (avg_ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[s.experts]
-        kname = "gemm_packed_kernel<%d, 0, false>" % {"bf16": 0, "fp8": 1, "fp4": 2}.get(s.experts, 0)
+        # the gate/up kernel the library launches for this layer (packed bf16
+        # weights: the one-wave-per-SIMD grouped GEMM)
+        if s.experts == "bf16":
+            kname = "gemm_grouped_bf16_kernel<0, false>"
+        else:
+            kname = "gemm_packed_kernel<%d, 0, false>" % {"fp8": 1, "fp4": 2}.get(s.experts, 0)
         traffic = recorded_traffic(s.name, kname) if layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
