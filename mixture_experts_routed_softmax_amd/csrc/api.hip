@@ -436,6 +436,8 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
                            (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), d->T <= 32, st);
   else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(act_rows, d->H))
     e = launch_gemm_grouped_bf16(a, act_rows, 0, grid, st);
+  else if (packed(d) && d->w_dtype == MOE_DT_FP8_E4M3 && gemm_grouped_fp8_fits(act_rows, d->H))
+    e = launch_gemm_grouped_fp8(a, act_rows, 0, grid, st);   // (measured faster than the packed kernel for gate/up only)
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);

@@ -117,6 +117,13 @@ hipError_t launch_gemm_packed(const GemmArgs& a, int wfmt, int mode, int grid, h
 // 4 GiB (32-bit row offsets); gemm_packed_kernel serves the rest.
 bool gemm_grouped_bf16_fits(int64_t act_rows, int K);
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream);
+// fp8 (e4m3, 128 x 128 block scales) grouped GEMM on packed weights with one
+// wave per SIMD, 128 token rows per tile; takes K a multiple of 128 up to
+// 128 * kStreamMaxScaleBlocks and activations spanning at most 4 GiB.
+// Gate/up only (mode 0): down stays on gemm_packed_kernel, which measured
+// faster at the DSv3-like K = 2048.
+bool gemm_grouped_fp8_fits(int64_t act_rows, int K);
+hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
 constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
 // weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per
