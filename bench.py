@@ -479,8 +479,10 @@ def main():
         # weights: the one-wave-per-SIMD grouped GEMM)
         if s.experts == "bf16":
             kname = "gemm_grouped_bf16_kernel<0, false>"
+        elif s.experts == "fp8":
+            kname = "gemm_grouped_fp8_kernel<0, false>"
         else:
-            kname = "gemm_packed_kernel<%d, 0, false>" % {"fp8": 1, "fp4": 2}.get(s.experts, 0)
+            kname = "gemm_packed_kernel<%d, 0, false>" % {"fp4": 2}.get(s.experts, 0)
         traffic = recorded_traffic(s.name, kname) if layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),

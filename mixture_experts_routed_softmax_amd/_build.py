@@ -28,9 +28,18 @@ CFLAGS = [
 ]
 
 
+# per-source code generation options
+#   gemm_grouped_fp8.hip: MFMA results in the architectural vector registers
+#   (the per-block promotion reads them with vector FMAs; in the accumulation
+#   registers every value would first need a copy)
+EXTRA_FLAGS = {
+    "gemm_grouped_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, r.stdout, r.stderr))

@@ -21,7 +21,7 @@
 // tokens, as 2 x 4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales).
 // A 128-deep scale block is two MFMAs deep: each tile's two MFMAs add into a
 // partial tile, which is folded into the fp32 accumulators with
-// s_w(block) s_x(row, block) (the promotion) token tile by token tile, so
+// s_w(block) s_x(row, block) (the promotion), tile by tile in a pipeline, so
 // that the vector unit's promotions run beside the matrix core's MFMAs.
 //
 // Weight rows are private to a wave and go from the packed chunks straight
@@ -233,51 +233,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (t + kTokAhead < KB) issue_t(t + kTokAhead, t + kTokAhead);
       if (t + kWAhead >= 0 && t + kWAhead < KB) load_w(ring[(t + kWAhead + kWSlots) % kWSlots], t + kWAhead);
     }
-    // one block: its tokens landed (this wave's DMA, then the barrier: every
-    // wave's, and the stage of block kb-1 is free), the next tops' loads
-    // issued; the first MFMA of every tile, then per token tile the second
-    // MFMAs and the promotion of the finished partial tiles with
-    // s_w(kb) * s_x(row, kb), so that the vector unit promotes one token tile
-    // while the matrix core runs the next one's MFMAs
-    // In the steady state (kb >= kTokAhead - kWAhead, so every earlier top
-    // issued in full, and kb + kTokAhead < KB) the wait is a compile-time
-    // count and the loads are issued without conditions, so that the
-    // compiler's own waits for the weight registers stay exact.
-    constexpr int kSteadyWait = kWLoads + (kTokAhead - 1) * (NT + kWLoads);
+    // token fragments of tile j, half h of the block in stage `stage`: row
+    // j*32 + l32, pieces 4h + hl and 4h + 2 + hl.  (Typed 16-byte loads, as
+    // in the bf16 kernel: the compiler then leaves their ordering against the
+    // token DMA to the explicit waits and barriers instead of waiting for
+    // every DMA in flight.)
+    auto frag = [&](int stage, int j, int h) {
+      const uint8_t* sb = smem + stage * kStage;
+      const bf16x8 lo = *(const bf16x8*)(sb + tswz(j * 32 + l32, 4 * h + hl));
+      const bf16x8 hi = *(const bf16x8*)(sb + tswz(j * 32 + l32, 4 * h + 2 + hl));
+      return join8(__builtin_bit_cast(i32x4, lo), __builtin_bit_cast(i32x4, hi));
+    };
+    // token fragments of two blocks: [parity][half][token tile]
+    i32x8 fb[2][2][NT];
+    // One block kb.  At its top this wave's DMA of block kb+1 has landed; the
+    // barrier then certifies every wave's, and that the stage of block kb-1
+    // (read during block kb-2) is free for the DMA of block kb + kTokAhead.
+    // The fragments of block kb were read during block kb-1; those of block
+    // kb+1 are read in the middle of this block's pipeline.  In the steady
+    // state (every earlier top issued in full, kb + kTokAhead < KB) the wait
+    // is a compile-time count and the loads are issued without conditions,
+    // so that the compiler's own waits for the weight registers stay exact.
+    constexpr int kSteadyWait = kWLoads + (kTokAhead - 2) * (NT + kWLoads);
     static_assert(kSteadyWait < 64, "vmcnt range");
-    auto block = [&](int kb, auto d_const, auto steady_const) {
+    auto block = [&](int kb, auto d_const, auto p_const, auto steady_const) {
       constexpr int d = decltype(d_const)::value;
+      constexpr int p = decltype(p_const)::value;
       constexpr bool kSteady = decltype(steady_const)::value;
       constexpr int df = (d + kWAhead) % kWSlots;
       if (kSteady) wait_vmcnt<kSteadyWait>();
-      else wait_vmcnt_le(ops_after(kb, kb - 1));
-      // a bare barrier: every wave's fragment reads of block kb-1 were
-      // consumed by its MFMAs, and each wave waited for its own DMA of block
-      // kb above (a workgroup fence here would wait for every DMA in flight)
+      else if (kb + 1 < KB) wait_vmcnt_le(ops_after(kb + 1, kb - 1));
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (kSteady || kb + kTokAhead < KB) issue_t((kb + kTokAhead) % kStages, kb + kTokAhead);
       if (kSteady || kb + kWAhead < KB) load_w(ring[df], kb + kWAhead);
-      const uint8_t* sb = smem + (kb % kStages) * kStage;
-      // token fragments of tile j, half h: row j*32 + l32, pieces 4h + hl and
-      // 4h + 2 + hl.  (Typed 16-byte loads, as in the bf16 kernel: the
-      // compiler then leaves the ordering against the token DMA to the
-      // explicit wait and barrier above instead of waiting for every DMA in
-      // flight.)
-      auto frag = [&](int j, int h) {
-        const bf16x8 lo = *(const bf16x8*)(sb + tswz(j * 32 + l32, 4 * h + hl));
-        const bf16x8 hi = *(const bf16x8*)(sb + tswz(j * 32 + l32, 4 * h + 2 + hl));
-        return join8(__builtin_bit_cast(i32x4, lo), __builtin_bit_cast(i32x4, hi));
-      };
       // gate/up: gate and up tiles; down: both tiles lie in row half wave >> 1
       const float sw0 = s_sw[kMode == 0 ? 0 : (wave >> 1)][kb];
       const float sw1 = s_sw[kMode == 0 ? 1 : (wave >> 1)][kb];
-      i32x8 b0[NT], b1[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) b0[j] = frag(j, 0);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) b1[j] = frag(j, 1);
       float m[2][NT];   // s_w(kb) * s_x(row, kb); lane holds token l32 of each token tile
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -285,54 +278,88 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         m[0][j] = sw0 * sx;
         m[1][j] = sw1 * sx;
       }
-      // Instruction order pinned: the first MFMA of every tile, then the
-      // second MFMA of tile k followed by the promotion of tile k-1 (whose
-      // second MFMA has finished meanwhile), so that the vector unit's
-      // promotions issue while the matrix core runs the next MFMA.
-      f32x16 part[2][NT];
+      // Instruction order pinned, a three-stage pipeline over the 2*NT tiles
+      // k = 2j + t: slot s issues the first MFMA of tile s, the second MFMA
+      // of tile s-1 and the promotion of tile s-2 (split around the second
+      // MFMA), so that each MFMA's input was finished two MFMAs earlier, the
+      // vector unit promotes while the matrix core runs, and only three
+      // tiles' partial sums are live (they fit the vector registers the
+      // promotion reads).  The next block's fragments are read at slot NT.
+      constexpr int NK = 2 * NT;
+      const int stn = (kb + 1) % kStages;
+      const bool next = kSteady || kb + 1 < KB;
+      f32x16 part[NK];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          part[t][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              join8(ring[d].a[t][0][0], ring[d].a[t][0][1]), b0[j], f32x16{}, 0, 0, 0, 127, 0, 127);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k <= 2 * NT; ++k) {
-        if (k < 2 * NT) {
-          const int j = k >> 1, t = k & 1;
-          part[t][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              join8(ring[d].a[t][1][0], ring[d].a[t][1][1]), b1[j], part[t][j], 0, 0, 0, 127, 0, 127);
+      for (int sl = 0; sl < NK + 2; ++sl) {
+        if (sl < NK) {
+          const int j = sl >> 1, t = sl & 1;
+          part[sl] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              join8(ring[d].a[t][0][0], ring[d].a[t][0][1]), fb[p][0][j], f32x16{}, 0, 0, 0, 127, 0, 127);
         }
-        if (k > 0) {
-          const int j = (k - 1) >> 1, t = (k - 1) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (sl >= 2) {
+          const int k = sl - 2, j = k >> 1, t = k & 1;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[t][j][r] = __builtin_fmaf(part[t][j][r], m[t][j], acc[t][j][r]);
+          for (int r = 0; r < 8; ++r) acc[t][j][r] = __builtin_fmaf(part[k][r], m[t][j], acc[t][j][r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (sl >= 1 && sl - 1 < NK) {
+          const int k = sl - 1, j = k >> 1, t = k & 1;
+          part[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              join8(ring[d].a[t][1][0], ring[d].a[t][1][1]), fb[p][1][j], part[k], 0, 0, 0, 127, 0, 127);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (sl >= 2) {
+          const int k = sl - 2, j = k >> 1, t = k & 1;
+#pragma unroll
+          for (int r = 8; r < 16; ++r) acc[t][j][r] = __builtin_fmaf(part[k][r], m[t][j], acc[t][j][r]);
+        }
+        if (sl == NT && next) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) fb[p ^ 1][h][j] = frag(stn, j, h);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    static_assert(kWSlots == 3 && kTokAhead - kWAhead == 3, "head of three blocks, loops unrolled by three");
-    constexpr std::integral_constant<int, 0> d0{};
-    constexpr std::integral_constant<int, 1> d1{};
-    constexpr std::integral_constant<int, 2> d2{};
+    constexpr std::integral_constant<int, 0> i0{};
+    constexpr std::integral_constant<int, 1> i1{};
+    constexpr std::integral_constant<int, 2> i2{};
     constexpr std::true_type steady{};
     constexpr std::false_type guarded{};
-    // head: blocks 0-2 (the prologue's tops issued no weights before block 0)
-    block(0, d0, guarded);
-    if (1 < KB) block(1, d1, guarded);
-    if (2 < KB) block(2, d2, guarded);
+    static_assert(kWSlots == 3 && kTokAhead - kWAhead == 3, "head of three blocks, loops unrolled by six");
+    // block 0's fragments, once its DMA landed for every wave
+    wait_vmcnt_le(ops_after(0, -1));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fb[0][h][j] = frag(0, j, h);
+    // head: blocks 0-2 (the prologue's tops issued no weights before block
+    // 0); weight slot kb % 3 and fragment parity kb % 2 stay compile-time
+    block(0, i0, i0, guarded);
+    if (1 < KB) block(1, i1, i1, guarded);
+    if (2 < KB) block(2, i2, i0, guarded);
     int kb = 3;
-    for (; kb + 2 + kTokAhead < KB; kb += 3) {
-      block(kb, d0, steady);
-      block(kb + 1, d1, steady);
-      block(kb + 2, d2, steady);
+    for (; kb + 5 + kTokAhead < KB; kb += 6) {
+      block(kb, i0, i1, steady);
+      block(kb + 1, i1, i0, steady);
+      block(kb + 2, i2, i1, steady);
+      block(kb + 3, i0, i0, steady);
+      block(kb + 4, i1, i1, steady);
+      block(kb + 5, i2, i0, steady);
     }
-    for (; kb < KB; kb += 3) {
-      block(kb, d0, guarded);
-      if (kb + 1 < KB) block(kb + 1, d1, guarded);
-      if (kb + 2 < KB) block(kb + 2, d2, guarded);
+    for (; kb < KB; kb += 6) {
+      block(kb, i0, i1, guarded);
+      if (kb + 1 < KB) block(kb + 1, i1, i0, guarded);
+      if (kb + 2 < KB) block(kb + 2, i2, i1, guarded);
+      if (kb + 3 < KB) block(kb + 3, i0, i0, guarded);
+      if (kb + 4 < KB) block(kb + 4, i1, i1, guarded);
+      if (kb + 5 < KB) block(kb + 5, i2, i0, guarded);
     }
   };
   switch (ntok) {
