@@ -170,6 +170,11 @@ size_t packed_bytes(const moe_desc* d, int which) {
 // I = 1408 157 vs 158-162 us).
 constexpr int kGroupedGateUpMinK = 4096;
 
+// prefill schedules: an expert's items in blocks of kSchedBlockM row tiles x
+// kSchedBlockN channel tiles, one block per XCD chunk of the grouped GEMMs
+constexpr int kSchedBlockM = 4;
+constexpr int kSchedBlockN = 4;
+
 // expert GEMMs stream the touched experts' weights (decode-sized batches)
 bool use_stream(const moe_desc* d) {
   if (is_fp8(d) && (d->H / 128 > kStreamMaxScaleBlocks || d->I / 128 > kStreamMaxScaleBlocks))
@@ -205,8 +210,9 @@ size_t stream_partial_bytes(const moe_desc* d) { return (size_t)stream_partial_u
 size_t sched_bytes(int64_t cap) { return sizeof(Schedule) + (size_t)cap * sizeof(WorkItem); }
 
 // grid covering every item index up to cap under xcd_work_index's mapping
-int grid_for(int64_t cap) {
-  const int64_t per = (int64_t)kNumXcd * kXcdChunk;
+// with chunks of `chunk` items
+int grid_for(int64_t cap, int chunk = kXcdChunk) {
+  const int64_t per = (int64_t)kNumXcd * chunk;
   return (int)((cap + per - 1) / per * per);
 }
 
@@ -374,6 +380,10 @@ SchedRequest sched_req(Schedule* s, const moe_desc* d, int ntiles) {
   r.rows_per_tile = rows_per_tile(d);
   r.ntiles = ntiles;
   r.capacity = (int)sched_capacity(d, ntiles);
+  if (!use_stream(d)) {
+    r.block_m = kSchedBlockM;
+    r.block_n = kSchedBlockN;
+  }
   return r;
 }
 
@@ -436,7 +446,7 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   a.wtiles = (int)packed_tiles(1, d->I);
   StageTimer tm(MOE_STAGE_GATE_UP, st);
   hipError_t e;
-  const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)));
+  const int grid = grid_for(sched_capacity(d, gate_up_ntiles(d)), kGroupedXcdChunk);
   const int64_t act_rows = gather ? d->T : pairs(d);   // x (read through perm) or x_sorted
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
@@ -475,7 +485,7 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
   a.wtiles = (int)packed_tiles(0, d->H);
   StageTimer tm(MOE_STAGE_DOWN, st);
   hipError_t e;
-  const int grid = grid_for(sched_capacity(d, down_ntiles(d)));
+  const int grid = grid_for(sched_capacity(d, down_ntiles(d)), kGroupedXcdChunk);
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 1, grid_for(stream_units_cap(sched_capacity(d, down_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, down_ntiles(d)), kStreamTarget), d->T <= 32, st,
@@ -521,6 +531,7 @@ int bwd_tiles(int64_t n) { return (int)((n + kBwdTile - 1) / kBwdTile); }
 SchedRequest bwd_sched_req(Schedule* s, const moe_desc* d, int ntiles) {
   SchedRequest r = sched_req(s, d, ntiles);
   r.rows_per_tile = kBwdTile;
+  r.block_m = r.block_n = 1;
   return r;
 }
 

@@ -76,17 +76,18 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 // XCD-aware work index of this workgroup.  Workgroups are dealt round-robin
-// to the 8 XCDs; work items are dealt to XCDs in chunks of kXcdChunk
-// consecutive items (consecutive items share an expert's weight tile, so a
-// chunk reuses it from one L2), and successive chunks go to successive XCDs
-// so that a hot expert's items spread over all of them.  Returns -1 for
-// workgroups beyond the live work.  gridDim.x is a multiple of
-// 8 * kXcdChunk covering every item index the schedule can hold.
+// to the 8 XCDs; work items are dealt to XCDs in chunks of C consecutive
+// items (consecutive items share an expert's weight tile or token rows, see
+// build_schedule, so a chunk reuses them from one L2), and successive chunks
+// go to successive XCDs so that a hot expert's items spread over all of them.
+// Returns -1 for workgroups beyond the live work.  gridDim.x is a multiple of
+// 8 * C covering every item index the schedule can hold.
 constexpr int kXcdChunk = 8;
+template <int C = kXcdChunk>
 __device__ __forceinline__ int xcd_work_index(int total) {
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
-  const int w = ((slot / kXcdChunk) * kNumXcd + xcd) * kXcdChunk + slot % kXcdChunk;
+  const int w = ((slot / C) * kNumXcd + xcd) * C + slot % C;
   return w < total ? w : -1;
 }
 

@@ -94,7 +94,7 @@ template <int kMode, bool kOutF32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_bf16_kernel(
     GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
-  const int w = xcd_work_index(a.sched->total);
+  const int w = xcd_work_index<kGroupedXcdChunk>(a.sched->total);
   if (w < 0) return;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
   const int tid = threadIdx.x, lane = tid & 63;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   float* s_sx = (float*)(smem + kStages * kStage);
   float (*s_sw)[kMaxKB] = (float (*)[kMaxKB])(s_sx + kMaxKB * kTok);
   float (*s_amax)[kTok] = (float (*)[kTok])(s_sx + kMaxKB * kTok + 2 * kMaxKB);
-  const int w = xcd_work_index(a.sched->total);
+  const int w = xcd_work_index<kGroupedXcdChunk>(a.sched->total);
   if (w < 0) return;
   const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
   const int tid = threadIdx.x, lane = tid & 63;

@@ -32,7 +32,13 @@ struct SchedRequest {
   int rows_per_tile;  // BM (token rows per tile)
   int ntiles;         // output-channel tiles per expert
   int capacity;       // items the buffer holds
+  int block_m = 1;    // an expert's items run in blocks of block_m row tiles
+  int block_n = 1;    //   x block_n channel tiles (see build_schedule)
 };
+
+// work items per XCD chunk of the one-wave-per-SIMD grouped GEMMs
+// (xcd_work_index<kGroupedXcdChunk>; their grid is a multiple of 8 times it)
+constexpr int kGroupedXcdChunk = 16;
 
 hipError_t launch_hist(const int32_t* ids, int64_t P, int E, int32_t* block_counts,
                        hipStream_t stream);

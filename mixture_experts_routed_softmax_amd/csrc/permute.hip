@@ -69,8 +69,13 @@ __device__ int block_exclusive_scan(int* v, int n, int* tmp) {
   return total;
 }
 
-// Fill one schedule: experts in ascending order, then output-channel tiles,
-// then row tiles (fastest), so that consecutive work items share weights.
+// Fill one schedule: experts in ascending order; inside an expert (M row
+// tiles x N output-channel tiles) blocks of up to block_m row tiles x block_n
+// channel tiles, the blocks channel-major, inside a block the channel tile
+// major and the row tile fastest.  Consecutive items then share a weight
+// tile, and a run of block_m * block_n items (one XCD chunk of the grouped
+// GEMMs) reads only block_n weight tiles and block_m token tiles.  With
+// block_m = block_n = 1 this is channel tile major, row tile fastest.
 __device__ void build_schedule(const int* s_offsets, int E, SchedRequest rq, int* s_tiles,
                                int* s_items, int* s_tmp) {
   const int tid = threadIdx.x;
@@ -95,10 +100,20 @@ __device__ void build_schedule(const int* s_offsets, int E, SchedRequest rq, int
       int mid = (lo + hi + 1) >> 1;
       if (s_items[mid] <= idx) lo = mid; else hi = mid - 1;
     }
-    int e = lo;
-    int local = idx - s_items[e];
-    int nt = local / s_tiles[e];
-    int mt = local - nt * s_tiles[e];
+    const int e = lo;
+    const int M = s_tiles[e];
+    const int bm = rq.block_m, bn = rq.block_n;
+    int r = idx - s_items[e];
+    // channel block: bn columns (the last one possibly fewer) of M row tiles
+    const int jb = r / (bn * M);
+    const int cols = min(bn, rq.ntiles - jb * bn);
+    r -= jb * bn * M;
+    // row block inside it: bm rows (the last one possibly fewer)
+    const int ib = r / (cols * bm);
+    const int rows = min(bm, M - ib * bm);
+    r -= ib * cols * bm;
+    const int nt = jb * bn + r / rows;
+    const int mt = ib * bm + r % rows;
     int rb = s_offsets[e] + mt * BM;
     int re = min(rb + BM, s_offsets[e + 1]);
     items[idx] = WorkItem{rb, re, e, nt};
