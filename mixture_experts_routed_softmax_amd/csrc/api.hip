@@ -878,14 +878,18 @@ static moe_status forward_impl(const moe_desc* d, const void* x, const void* w_r
   if ((s = run_gate_up(d, act, act_scales, fw.perm, fw.offsets, w_gate, w_up, sg, su, fw.h, fw.hs, fw.sched_gu, fw.partial,
                        st)) != MOE_OK)
     return s;
-  // Weight streaming: when even the most items the batch can touch leave the
-  // down launch unsplit (the usual case), its reduction launch is left out and
-  // the combine reads y, or sums the partial tiles should fewer experts make
-  // it split after all.  (With few items the reduction launch spreads the
-  // partial sums over many CUs, where a combine workgroup per token would not.)
+  // Weight streaming: the down launch's reduction launch is left out and the
+  // combine reads y, or sums the partial tiles of a split launch, when
+  //  - the batch is small enough for the combine's fine decomposition (one
+  //    workgroup per token and 32 channels reads the partials in parallel), or
+  //  - even the most items the batch can touch leave the down launch unsplit
+  //    (then a split is rare, and a combine workgroup per token and 2048
+  //    channels sums the partials).
   const int64_t dn_items_max = std::min<int64_t>(d->E, P) * down_ntiles(d);
-  if (use_stream(d) && stream_splits((int)std::min<int64_t>(dn_items_max, 1 << 30), stream_ksteps(wfmt(d), d->I),
-                                     stream_slots(wfmt(d), d->T <= 32)) == 1) {
+  if (use_stream(d) &&
+      ((d->T <= kCombineFineMaxT && d->H % 32 == 0) ||
+       stream_splits((int)std::min<int64_t>(dn_items_max, 1 << 30), stream_ksteps(wfmt(d), d->I),
+                     stream_slots(wfmt(d), d->T <= 32)) == 1)) {
     if ((s = run_down(d, fw.h, fw.hs, fw.offsets, w_down, sd, fw.y, fw.sched_dn, fw.partial, st, fw.rowinfo)) !=
         MOE_OK)
       return s;

@@ -180,17 +180,122 @@ __global__ __launch_bounds__(256) void combine_split_kernel(const void* __restri
   }
 }
 
+// The same combine for small batches, where a split down launch leaves up to
+// k * 16 partial rows per token: one workgroup per (token, 32 channels), so
+// that the partial reads spread over many CUs.  Thread (q, g) loads the 8
+// channels g of (slot, split) pair q = slot * S + split into LDS, a chunk of
+// slots at a time; thread c < 32 then sums channel c of each slot over its
+// splits in split order, rounds to y's type and accumulates the slots in slot
+// order, exactly as combine_split_kernel does.
+constexpr int kFineChannels = 32;
+constexpr int kFinePairs = 128;   // (slot, split) pairs staged in LDS at once
+
+template <bool kYF32, bool kOutF32>
+__global__ __launch_bounds__(256) void combine_split_fine_kernel(const void* __restrict__ y,
+                                                                 const float* __restrict__ partial,
+                                                                 const int32_t* __restrict__ rowinfo,
+                                                                 const Schedule* __restrict__ sched, int ksteps,
+                                                                 int slots, const int32_t* __restrict__ inv,
+                                                                 const float* __restrict__ w, int k, int H,
+                                                                 void* __restrict__ out) {
+  __shared__ int s_row[kMaxTopK];
+  __shared__ int s_info[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
+  __shared__ float s_v[kFinePairs][kFineChannels];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int S = stream_splits(sched->total, ksteps, slots);
+  if (tid < k) {
+    const int64_t row = inv[t * k + tid];
+    const bool ok = row >= 0 && row < (int64_t)gridDim.x * k;
+    s_row[tid] = ok ? (int)row : -1;
+    s_info[tid] = ok && S > 1 ? rowinfo[row] : 0;
+    s_w[tid] = w[t * k + tid];
+  }
+  __syncthreads();
+  const int ch0 = blockIdx.y * kFineChannels;         // first channel of this workgroup
+  const int g = tid & 3;                              // 8-channel group of this thread
+  const int c8 = ch0 / 8 + g;                         // global group of 8 channels
+  const int nt = c8 / 32, cc = (c8 % 32) * 8;         // channel tile, channel within it
+  const int kc = kFinePairs / S < k ? kFinePairs / S : k;   // slots per chunk (S <= 16)
+  float acc = 0.f;
+  for (int i0 = 0; i0 < k; i0 += kc) {
+    const int npairs = (k - i0 < kc ? k - i0 : kc) * S;
+    for (int q = tid >> 2; q < npairs; q += 64) {
+      const int i = i0 + q / S, sp = q % S;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (s_row[i] >= 0) {
+        if (S == 1) {
+          const int64_t base = (int64_t)s_row[i] * H + c8 * 8;
+          if (kYF32) {
+            const f32x4 v0 = *(const f32x4*)((const float*)y + base);
+            const f32x4 v1 = *(const f32x4*)((const float*)y + base + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[j] = v0[j];
+              v[4 + j] = v1[j];
+            }
+          } else {
+            const i32x4 b = *(const i32x4*)((const uint16_t*)y + base);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[2 * j] = bf16_bits_to_f32((uint16_t)((uint32_t)b[j] & 0xffff));
+              v[2 * j + 1] = bf16_bits_to_f32((uint16_t)((uint32_t)b[j] >> 16));
+            }
+          }
+        } else {
+          const int info = s_info[i];
+          const float* p = partial + ((int64_t)(info / 64 + nt) * S + sp) * kStreamPartFloats + (info % 64) * 256 + cc;
+          const f32x4 v0 = *(const f32x4*)p;
+          const f32x4 v1 = *(const f32x4*)(p + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = v0[j];
+            v[4 + j] = v1[j];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_v[q][g * 8 + j] = v[j];
+    }
+    __syncthreads();
+    if (tid < kFineChannels) {
+      for (int ii = 0; ii < npairs / S; ++ii) {
+        const int i = i0 + ii;
+        if (s_row[i] < 0) continue;
+        float v = 0.f;
+        for (int sp = 0; sp < S; ++sp) v += s_v[ii * S + sp][tid];
+        if (!kYF32 && S > 1) v = bf16_bits_to_f32(f32_to_bf16_bits(v));
+        acc = __builtin_fmaf(s_w[i], v, acc);
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < kFineChannels) {
+    const int64_t o = t * H + ch0 + tid;
+    if (kOutF32) ((float*)out)[o] = acc;
+    else ((uint16_t*)out)[o] = f32_to_bf16_bits(acc);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine_stream(const void* y, int y_f32, const float* partial, const int32_t* rowinfo,
                                  const Schedule* sched, int ksteps, int slots, const int32_t* inv, const float* w,
                                  int64_t T, int k, int H, void* out, int out_f32, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (H % 8 != 0) return hipErrorInvalidValue;
-  dim3 grid((unsigned)T, (unsigned)((H / 8 + 255) / 256)), block(256);
-#define MOE_COMBINE_SPLIT(YF, OF)                                                                        \
-  hipLaunchKernelGGL((combine_split_kernel<YF, OF>), grid, block, 0, stream, y, partial, rowinfo, sched, \
-                     ksteps, slots, inv, w, k, H, out)
+  if (H % 8 != 0 || k > kMaxTopK) return hipErrorInvalidValue;
+  const bool fine = T <= kCombineFineMaxT && H % kFineChannels == 0;
+  dim3 grid((unsigned)T, (unsigned)(fine ? H / kFineChannels : (H / 8 + 255) / 256)), block(256);
+#define MOE_COMBINE_SPLIT(YF, OF)                                                                          \
+  do {                                                                                                     \
+    if (fine)                                                                                              \
+      hipLaunchKernelGGL((combine_split_fine_kernel<YF, OF>), grid, block, 0, stream, y, partial, rowinfo, \
+                         sched, ksteps, slots, inv, w, k, H, out);                                        \
+    else                                                                                                   \
+      hipLaunchKernelGGL((combine_split_kernel<YF, OF>), grid, block, 0, stream, y, partial, rowinfo,      \
+                         sched, ksteps, slots, inv, w, k, H, out);                                        \
+  } while (0)
   if (y_f32 && out_f32) MOE_COMBINE_SPLIT(true, true);
   else if (y_f32) MOE_COMBINE_SPLIT(true, false);
   else if (out_f32) MOE_COMBINE_SPLIT(false, true);

@@ -36,7 +36,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN)
 // fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);

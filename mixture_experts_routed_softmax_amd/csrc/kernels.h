@@ -243,6 +243,10 @@ hipError_t launch_combine(const void* y, int y_f32, const int32_t* inv, const fl
 // after a streaming down launch without its reduction: y rows from y when the
 // launch was not split, else summed from its partial tiles (split order) and
 // rounded to y's type first; then the combine above, same arithmetic
+// Batches of at most kCombineFineMaxT tokens take one workgroup per (token, 32
+// channels) when H is a multiple of 32, whose threads read the (slot, split)
+// partial rows in parallel.
+constexpr int kCombineFineMaxT = 16;
 hipError_t launch_combine_stream(const void* y, int y_f32, const float* partial, const int32_t* rowinfo,
                                  const Schedule* sched, int ksteps, int slots, const int32_t* inv, const float* w,
                                  int64_t T, int k, int H, void* out, int out_f32, hipStream_t stream);

@@ -12,7 +12,7 @@
 //   hist    : per-chunk expert histograms (chunks of 1024 pairs)
 //   scan    : counts, offsets, per-chunk bases (offsets + earlier chunks), the
 //             touched-expert list and the grouped-GEMM work schedules
-//   scatter : stable in-chunk ranks (wave readlane scan + per-wave counts)
+//   scatter : stable in-chunk ranks (wave ballots per distinct id + per-wave counts)
 // or, when all pairs fit one chunk, a single workgroup that does all three.
 #include "common.h"
 #include "kernels.h"
@@ -41,69 +41,89 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
     block_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
 }
 
-// In-place exclusive scan of v[0..n) (n <= 1024) by the whole 1024-thread block;
-// returns the total.  v must be in LDS; tmp is LDS scratch of at least 16 ints.
-// Each wave scans its 64 entries with lane shuffles, then the 16 wave totals
-// are scanned the same way by every wave.
-__device__ int block_exclusive_scan(int* v, int n, int* tmp) {
+// In-place exclusive scans of N arrays v[j][0..n) (n <= 1024) by the whole
+// 1024-thread block; total[j] gets each array's sum.  The arrays must be in
+// LDS; tmp is LDS scratch of at least 16 * N ints.  Each wave scans its 64
+// entries with lane shuffles, then the 16 wave totals are scanned the same way
+// by every wave.  Scanning several arrays together costs one pair of barriers.
+template <int N>
+__device__ void block_exclusive_scan_n(int* const (&v)[N], int n, int* tmp, int (&total)[N]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int x = tid < n ? v[tid] : 0;
-  int inc = x;
+  int x[N], inc[N];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  int wt = lane < 16 ? tmp[lane] : 0;   // wave totals, scanned inclusively
+  for (int j = 0; j < N; ++j) inc[j] = x[j] = tid < n ? v[j][tid] : 0;
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    const int y = __shfl_up(wt, off);
-    if (lane >= off) wt += y;
-  }
-  const int before = wave > 0 ? __shfl(wt, wave - 1) : 0;
-  const int total = __shfl(wt, 15);
-  if (tid < n) v[tid] = before + inc - x;
+  for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int y = __shfl_up(inc[j], off);
+      if (lane >= off) inc[j] += y;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int j = 0; j < N; ++j) tmp[16 * j + wave] = inc[j];
   __syncthreads();
-  return total;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    int wt = lane < 16 ? tmp[16 * j + lane] : 0;   // wave totals, scanned inclusively
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(wt, off);
+      if (lane >= off) wt += y;
+    }
+    const int before = wave > 0 ? __shfl(wt, wave - 1) : 0;
+    total[j] = __shfl(wt, 15);
+    if (tid < n) v[j][tid] = before + inc[j] - x[j];
+  }
+  __syncthreads();
 }
 
-// Fill one schedule: experts in ascending order; inside an expert (M row
+__device__ int block_exclusive_scan(int* v, int n, int* tmp) {
+  int* const arrays[1] = {v};
+  int total[1];
+  block_exclusive_scan_n<1>(arrays, n, tmp, total);
+  return total[0];
+}
+
+// Rank of this lane's id among the earlier lanes of its wave holding the same
+// id: one round per distinct id in the wave (a wave of decode-sized batches
+// holds few).
+__device__ __forceinline__ int wave_rank_same(int e, int lane) {
+  int rank = 0;
+  uint64_t todo = ~0ull;
+  while (todo != 0) {
+    const int leader = __builtin_ctzll(todo);
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t same = __ballot(e == el);
+    if (e == el) rank = __popcll(same & ((1ull << lane) - 1ull));
+    todo &= ~same;
+  }
+  return rank;
+}
+
+// Items of one schedule: experts in ascending order; inside an expert (M row
 // tiles x N output-channel tiles) blocks of up to block_m row tiles x block_n
 // channel tiles, the blocks channel-major, inside a block the channel tile
 // major and the row tile fastest.  Consecutive items then share a weight
 // tile, and a run of block_m * block_n items (one XCD chunk of the grouped
 // GEMMs) reads only block_n weight tiles and block_m token tiles.  With
 // block_m = block_n = 1 this is channel tile major, row tile fastest.
-__device__ void build_schedule(const int* s_offsets, int E, SchedRequest rq, int* s_tiles,
-                               int* s_items, int* s_tmp) {
-  const int tid = threadIdx.x;
+// s_tiles[e]: row tiles of expert e; s_base[e]: its first item.
+__device__ void write_schedule_items(const int* s_offsets, int E, SchedRequest rq, const int* s_tiles,
+                                     const int* s_base, int total) {
   const int BM = rq.rows_per_tile;
-  for (int e = tid; e < E; e += 1024) {
-    int c = s_offsets[e + 1] - s_offsets[e];
-    s_tiles[e] = (c + BM - 1) / BM;
-    s_items[e] = s_tiles[e] * rq.ntiles;
-  }
-  __syncthreads();
-  int total = block_exclusive_scan(s_items, E, s_tmp);   // s_items -> item bases
-  if (tid == 0) {
-    s_items[E] = total;
-    rq.sched->total = total;
-  }
-  __syncthreads();
   WorkItem* items = (WorkItem*)(rq.sched + 1);
-  for (int idx = tid; idx < total; idx += 1024) {
+  for (int idx = threadIdx.x; idx < total; idx += 1024) {
     // largest e with base[e] <= idx
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (s_items[mid] <= idx) lo = mid; else hi = mid - 1;
+      if (s_base[mid] <= idx) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
     const int M = s_tiles[e];
     const int bm = rq.block_m, bn = rq.block_n;
-    int r = idx - s_items[e];
+    int r = idx - s_base[e];
     // channel block: bn columns (the last one possibly fewer) of M row tiles
     const int jb = r / (bn * M);
     const int cols = min(bn, rq.ntiles - jb * bn);
@@ -114,11 +134,52 @@ __device__ void build_schedule(const int* s_offsets, int E, SchedRequest rq, int
     r -= ib * cols * bm;
     const int nt = jb * bn + r / rows;
     const int mt = ib * bm + r % rows;
-    int rb = s_offsets[e] + mt * BM;
-    int re = min(rb + BM, s_offsets[e + 1]);
+    const int rb = s_offsets[e] + mt * BM;
+    const int re = min(rb + BM, s_offsets[e + 1]);
     items[idx] = WorkItem{rb, re, e, nt};
   }
+}
+
+// LDS scratch of build_touched_and_schedules, in ints
+constexpr int kSchedWork = 5 * (kMaxExperts + 1);
+
+// From the expert offsets (in LDS): the touched-expert list (ascending, its
+// length in touched[E]; touched may be null) and up to two grouped-GEMM
+// schedules (a null sched skips one), with a single three-way scan.
+__device__ void build_touched_and_schedules(const int* s_offsets, int E, int32_t* __restrict__ touched,
+                                            SchedRequest s0, SchedRequest s1, int* s_work, int* s_tmp) {
+  const int tid = threadIdx.x;
+  int* s_tiles0 = s_work;
+  int* s_tiles1 = s_work + (kMaxExperts + 1);
+  int* s_base0 = s_work + 2 * (kMaxExperts + 1);
+  int* s_base1 = s_work + 3 * (kMaxExperts + 1);
+  int* s_tpos = s_work + 4 * (kMaxExperts + 1);
+  for (int e = tid; e < E; e += 1024) {
+    const int c = s_offsets[e + 1] - s_offsets[e];
+    const int m0 = s0.sched != nullptr ? (c + s0.rows_per_tile - 1) / s0.rows_per_tile : 0;
+    const int m1 = s1.sched != nullptr ? (c + s1.rows_per_tile - 1) / s1.rows_per_tile : 0;
+    s_tiles0[e] = m0;
+    s_base0[e] = m0 * s0.ntiles;
+    s_tiles1[e] = m1;
+    s_base1[e] = m1 * s1.ntiles;
+    s_tpos[e] = c > 0 ? 1 : 0;
+  }
   __syncthreads();
+  int* const arrays[3] = {s_base0, s_base1, s_tpos};
+  int total[3];
+  block_exclusive_scan_n<3>(arrays, E, s_tmp, total);
+  if (touched != nullptr) {
+    if (tid < E && s_offsets[tid + 1] > s_offsets[tid]) touched[s_tpos[tid]] = tid;
+    if (tid == 0) touched[E] = total[2];
+  }
+  if (s0.sched != nullptr) {
+    if (tid == 0) s0.sched->total = total[0];
+    write_schedule_items(s_offsets, E, s0, s_tiles0, s_base0, total[0]);
+  }
+  if (s1.sched != nullptr) {
+    if (tid == 0) s1.sched->total = total[1];
+    write_schedule_items(s_offsets, E, s1, s_tiles1, s_base1, total[1]);
+  }
 }
 
 __global__ __launch_bounds__(1024) void scan_kernel(
@@ -127,8 +188,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     SchedRequest s0, SchedRequest s1) {
   __shared__ int s_part[4][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
-  __shared__ int s_tiles[kMaxExperts];
-  __shared__ int s_items[kMaxExperts + 1];
+  __shared__ int s_work[kSchedWork];
   __shared__ int s_tmp[1024];
   const int tid = threadIdx.x;
   const int e = tid & 255;
@@ -174,17 +234,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
         }
     }
   }
-  // touched experts, ascending, count in touched[E]
-  if (touched != nullptr) {
-    if (tid < E) s_tiles[tid] = (s_offsets[tid + 1] - s_offsets[tid]) > 0 ? 1 : 0;
-    __syncthreads();
-    int U = block_exclusive_scan(s_tiles, E, s_tmp);
-    if (tid < E && s_offsets[tid + 1] > s_offsets[tid]) touched[s_tiles[tid]] = tid;
-    if (tid == 0) touched[E] = U;
-    __syncthreads();
-  }
-  if (s0.sched != nullptr) build_schedule(s_offsets, E, s0, s_tiles, s_items, s_tmp);
-  if (s1.sched != nullptr) build_schedule(s_offsets, E, s1, s_tiles, s_items, s_tmp);
+  build_touched_and_schedules(s_offsets, E, touched, s0, s1, s_work, s_tmp);
 }
 
 // All of the above in one workgroup when the pairs fit one chunk (P <= 1024,
@@ -198,20 +248,14 @@ __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ co
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_wcount[16][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
-  __shared__ int s_tiles[kMaxExperts];
-  __shared__ int s_items[kMaxExperts + 1];
+  __shared__ int s_work[kSchedWork];
   __shared__ int s_tmp[1024];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int x = tid; x < E; x += 1024) s_cnt[x] = 0;
   for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
   __syncthreads();
   if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
-  // rank among earlier lanes of this wave with the same expert
-  int rank = 0;
-  for (int j = 0; j < 64; ++j) {
-    const int ej = __builtin_amdgcn_readlane(e, j);
-    rank += (j < lane && ej == e) ? 1 : 0;
-  }
+  const int rank = wave_rank_same(e, lane);
   if (e >= 0) {
     atomicAdd(&s_cnt[e], 1);
     atomicAdd(&s_wcount[wave][e], 1);
@@ -234,16 +278,7 @@ __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ co
   } else if (tid < P) {
     inv[tid] = -1;   // a pair with an out-of-range id has no row
   }
-  if (touched != nullptr) {
-    if (tid < E) s_tiles[tid] = (s_offsets[tid + 1] - s_offsets[tid]) > 0 ? 1 : 0;
-    __syncthreads();
-    const int U = block_exclusive_scan(s_tiles, E, s_tmp);
-    if (tid < E && s_offsets[tid + 1] > s_offsets[tid]) touched[s_tiles[tid]] = tid;
-    if (tid == 0) touched[E] = U;
-    __syncthreads();
-  }
-  if (s0.sched != nullptr) build_schedule(s_offsets, E, s0, s_tiles, s_items, s_tmp);
-  if (s1.sched != nullptr) build_schedule(s_offsets, E, s1, s_tiles, s_items, s_tmp);
+  build_touched_and_schedules(s_offsets, E, touched, s0, s1, s_work, s_tmp);
 }
 
 __global__ __launch_bounds__(1024) void permute_small_kernel(
@@ -281,12 +316,11 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         SchedRequest rq) {
   __shared__ int s_offsets[kMaxExperts + 1];
-  __shared__ int s_tiles[kMaxExperts];
-  __shared__ int s_items[kMaxExperts + 1];
+  __shared__ int s_work[kSchedWork];
   __shared__ int s_tmp[1024];
   for (int i = threadIdx.x; i <= E; i += 1024) s_offsets[i] = offsets[i];
   __syncthreads();
-  build_schedule(s_offsets, E, rq, s_tiles, s_items, s_tmp);
+  build_touched_and_schedules(s_offsets, E, nullptr, rq, SchedRequest{}, s_work, s_tmp);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
@@ -315,12 +349,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     int e = ids_r[round];
     if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
     const bool valid = e >= 0;
-    // rank among earlier lanes of this wave with the same expert
-    int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-      int ej = __builtin_amdgcn_readlane(e, j);
-      rank += (j < lane && ej == e) ? 1 : 0;
-    }
+    const int rank = wave_rank_same(e, lane);
     if (valid) atomicAdd(&s_wcount[wave][e], 1);
     __syncthreads();
     if (valid) {

@@ -20,6 +20,49 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// Wave reductions with DPP lane moves instead of LDS-routed shuffles: xor 1
+// and xor 2 inside quads, mirrors inside half rows and rows (each lane then
+// holds its row's result), the row broadcasts of lanes 15 and 31 (row 3 then
+// holds the wave's), and a read of lane 63, so every lane gets the same value.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void argmax_step(float& bk, int& bi) {
+  const float ok = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bk), __float_as_int(bk), kCtrl,
+                                                              kRowMask, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, kCtrl, kRowMask, 0xf, false);
+  if (better(ok, oi, bk, bi)) {
+    bk = ok;
+    bi = oi;
+  }
+}
+
+// (key, index) of the wave's best lane: larger key, ties to the lower index
+__device__ __forceinline__ void wave_argmax(float& bk, int& bi) {
+  argmax_step<0xb1, 0xf>(bk, bi);    // quad_perm [1,0,3,2]
+  argmax_step<0x4e, 0xf>(bk, bi);    // quad_perm [2,3,0,1]
+  argmax_step<0x141, 0xf>(bk, bi);   // row_half_mirror
+  argmax_step<0x140, 0xf>(bk, bi);   // row_mirror
+  argmax_step<0x142, 0xa>(bk, bi);   // row_bcast:15 into rows 1 and 3
+  argmax_step<0x143, 0xc>(bk, bi);   // row_bcast:31 into rows 2 and 3
+  bk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bk), 63));
+  bi = __builtin_amdgcn_readlane(bi, 63);
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float sum_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, false));
+}
+
+// sum over the wave (a fixed order: the same value in every lane)
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum_step<0xb1, 0xf>(v);
+  v = sum_step<0x4e, 0xf>(v);
+  v = sum_step<0x141, 0xf>(v);
+  v = sum_step<0x140, 0xf>(v);
+  v = sum_step<0x142, 0xa>(v);
+  v = sum_step<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Top-k of one token's keys held by a wave (lane l owns experts l, l+64,
 // l+128, l+192): k rounds of a 64-lane argmax (larger key wins, ties to the
 // lower index), then the scores and routing weights; lane i < k writes slot i.
@@ -35,12 +78,7 @@ __device__ __forceinline__ void select_topk(float (&key)[4], bool (&taken)[4], i
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (!taken[q] && better(key[q], lane + 64 * q, bk, bi)) { bk = key[q]; bi = lane + 64 * q; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ok = __shfl_xor(bk, off);
-      int oi = __shfl_xor(bi, off);
-      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
-    }
+    wave_argmax(bk, bi);
     if ((bi & 63) == lane) taken[bi >> 6] = true;
     if (lane == i) { my_key = bk; my_idx = bi; }
     if (i == 0) kmax = bk;
@@ -51,17 +89,12 @@ __device__ __forceinline__ void select_topk(float (&key)[4], bool (&taken)[4], i
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (lane + 64 * q < E) part += expf(key[q] - kmax);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    s = expf(my_key - kmax) / part;
+    s = expf(my_key - kmax) / wave_sum(part);
   } else {
     s = 1.0f / (1.0f + expf(-my_key));
   }
   if (renorm) {
-    float sum = lane < k ? s : 0.f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    s = s / sum;
+    s = s / wave_sum(lane < k ? s : 0.f);
   }
   if (lane < k) {
     ids_out[lane] = my_idx;

@@ -328,6 +328,30 @@ def test_stream_combine_sums_down_partials(y_dtype):
     assert err <= tol_of(s)
 
 
+# batches of at most 16 tokens: the combine takes one workgroup per (token, 32
+# channels) and sums a split down launch's partial tiles itself
+FINE = {
+    # 16 slots x 16 splits: two chunks of (slot, split) pairs in LDS
+    "t1_k16_split": synthetic.spec("qwen_decode", T=1, H=512, I=2048, E=64, k=16),
+    # enough touched experts that the down launch is not split: y is read
+    "t16_unsplit": synthetic.spec("dsv3_bf16", T=16, H=2048, I=256, E=256, k=8),
+}
+
+
+@pytest.mark.parametrize("y_dtype", [None, "f32"])
+@pytest.mark.parametrize("name", list(FINE))
+def test_stream_fine_combine(name, y_dtype):
+    s = FINE[name]
+    L, hl = _layer(s, seed=23)
+    ids_o, w_o = oracle_route(s, hl)
+    out, ids, w, counts = run_forward(s, L, path="stream", y_dtype=y_dtype, layout="packed")
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    out_o = oracle_experts(s, hl).combine(hl["x"], ids_o, w_o)
+    err = row_rel_err(out.cpu().float().numpy(), out_o)
+    print("%s fine combine (y %s): max row rel err %.3e" % (name, y_dtype, err))
+    assert err <= tol_of(s)
+
+
 @pytest.mark.parametrize("name", ["bf16_decode", "fp8_decode_f32"])
 def test_stream_staged_matches_oracle(name):
     s = STREAM[name]
