@@ -41,48 +41,50 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
     block_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
 }
 
-// In-place exclusive scans of N arrays v[j][0..n) (n <= 1024) by the whole
-// 1024-thread block; total[j] gets each array's sum.  The arrays must be in
-// LDS; tmp is LDS scratch of at least 16 * N ints.  Each wave scans its 64
-// entries with lane shuffles, then the 16 wave totals are scanned the same way
-// by every wave.  Scanning several arrays together costs one pair of barriers.
-template <int N>
-__device__ void block_exclusive_scan_n(int* const (&v)[N], int n, int* tmp, int (&total)[N]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int x[N], inc[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) inc[j] = x[j] = tid < n ? v[j][tid] : 0;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1)
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int y = __shfl_up(inc[j], off);
-      if (lane >= off) inc[j] += y;
-    }
-  if (lane == 63)
-#pragma unroll
-    for (int j = 0; j < N; ++j) tmp[16 * j + wave] = inc[j];
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    int wt = lane < 16 ? tmp[16 * j + lane] : 0;   // wave totals, scanned inclusively
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int y = __shfl_up(wt, off);
-      if (lane >= off) wt += y;
-    }
-    const int before = wave > 0 ? __shfl(wt, wave - 1) : 0;
-    total[j] = __shfl(wt, 15);
-    if (tid < n) v[j][tid] = before + inc[j] - x[j];
-  }
-  __syncthreads();
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// shifts by 1, 2, 4 and 8 inside rows of 16 lanes, then the row broadcasts of
+// lanes 15 and 31 carry the earlier rows' totals forward.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int scan_step(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, true);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = scan_step<0x111, 0xf>(v);   // row_shr:1
+  v = scan_step<0x112, 0xf>(v);   // row_shr:2
+  v = scan_step<0x114, 0xf>(v);   // row_shr:4
+  v = scan_step<0x118, 0xf>(v);   // row_shr:8
+  v = scan_step<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = scan_step<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
-__device__ int block_exclusive_scan(int* v, int n, int* tmp) {
-  int* const arrays[1] = {v};
-  int total[1];
-  block_exclusive_scan_n<1>(arrays, n, tmp, total);
-  return total[0];
+// In-place exclusive scans of N arrays v[j][0..n) (n <= 256) in LDS by the
+// first wave of the block (lane l: entries 4l .. 4l+3), then a barrier of the
+// whole block; total[j] gets each array's sum in every thread.  The arrays'
+// entries must be written before (with a barrier); tmp: LDS scratch of N ints.
+template <int N>
+__device__ void block_exclusive_scan_n(int* const (&v)[N], int n, int* tmp, int (&total)[N]) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      int x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = 4 * lane + q < n ? v[j][4 * lane + q] : 0;
+      const int t = x[0] + x[1] + x[2] + x[3];
+      const int inc = wave_inclusive_scan(t);
+      int run = inc - t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * lane + q < n) v[j][4 * lane + q] = run;
+        run += x[q];
+      }
+      if (lane == 63) tmp[j] = inc;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < N; ++j) total[j] = tmp[j];
 }
 
 // Rank of this lane's id among the earlier lanes of its wave holding the same
@@ -101,29 +103,32 @@ __device__ __forceinline__ int wave_rank_same(int e, int lane) {
   return rank;
 }
 
-// Items of one schedule: experts in ascending order; inside an expert (M row
-// tiles x N output-channel tiles) blocks of up to block_m row tiles x block_n
-// channel tiles, the blocks channel-major, inside a block the channel tile
-// major and the row tile fastest.  Consecutive items then share a weight
+// Item idx of one schedule: experts in ascending order; inside an expert (M
+// row tiles x N output-channel tiles) blocks of up to block_m row tiles x
+// block_n channel tiles, the blocks channel-major, inside a block the channel
+// tile major and the row tile fastest.  Consecutive items then share a weight
 // tile, and a run of block_m * block_n items (one XCD chunk of the grouped
 // GEMMs) reads only block_n weight tiles and block_m token tiles.  With
 // block_m = block_n = 1 this is channel tile major, row tile fastest.
-// s_tiles[e]: row tiles of expert e; s_base[e]: its first item.
-__device__ void write_schedule_items(const int* s_offsets, int E, SchedRequest rq, const int* s_tiles,
-                                     const int* s_base, int total) {
-  const int BM = rq.rows_per_tile;
-  WorkItem* items = (WorkItem*)(rq.sched + 1);
-  for (int idx = threadIdx.x; idx < total; idx += 1024) {
-    // largest e with base[e] <= idx
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_base[mid] <= idx) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int M = s_tiles[e];
-    const int bm = rq.block_m, bn = rq.block_n;
-    int r = idx - s_base[e];
+// s_tiles[e]: row tiles of expert e; s_base[e]: its first item; rows_total:
+// the row count (the end of the last expert's rows).
+__device__ void write_schedule_item(const int* s_offsets, int E, int rows_total, SchedRequest rq,
+                                    const int* s_tiles, const int* s_base, int idx) {
+  // largest e with base[e] <= idx
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_base[mid] <= idx) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int M = s_tiles[e];
+  const int bm = rq.block_m, bn = rq.block_n;
+  int r = idx - s_base[e];
+  int nt, mt;
+  if (bm == 1 && bn == 1) {
+    nt = r / M;
+    mt = r - nt * M;
+  } else {
     // channel block: bn columns (the last one possibly fewer) of M row tiles
     const int jb = r / (bn * M);
     const int cols = min(bn, rq.ntiles - jb * bn);
@@ -132,32 +137,40 @@ __device__ void write_schedule_items(const int* s_offsets, int E, SchedRequest r
     const int ib = r / (cols * bm);
     const int rows = min(bm, M - ib * bm);
     r -= ib * cols * bm;
-    const int nt = jb * bn + r / rows;
-    const int mt = ib * bm + r % rows;
-    const int rb = s_offsets[e] + mt * BM;
-    const int re = min(rb + BM, s_offsets[e + 1]);
-    items[idx] = WorkItem{rb, re, e, nt};
+    nt = jb * bn + r / rows;
+    mt = ib * bm + r % rows;
   }
+  const int BM = rq.rows_per_tile;
+  const int rb = s_offsets[e] + mt * BM;
+  const int re = min(rb + BM, e + 1 < E ? s_offsets[e + 1] : rows_total);
+  ((WorkItem*)(rq.sched + 1))[idx] = WorkItem{rb, re, e, nt};
 }
 
-// LDS scratch of build_touched_and_schedules, in ints
-constexpr int kSchedWork = 5 * (kMaxExperts + 1);
+// LDS scratch of scan_counts_and_schedules, in ints
+constexpr int kSchedWork = 6 * (kMaxExperts + 1);
 
-// From the expert offsets (in LDS): the touched-expert list (ascending, its
-// length in touched[E]; touched may be null) and up to two grouped-GEMM
-// schedules (a null sched skips one), with a single three-way scan.
-__device__ void build_touched_and_schedules(const int* s_offsets, int E, int32_t* __restrict__ touched,
-                                            SchedRequest s0, SchedRequest s1, int* s_work, int* s_tmp) {
+// From the expert counts s_cnt[0..E) (LDS, may be s_offsets itself): the
+// exclusive offsets in s_offsets[0..E) and their total (the row count, also
+// stored at s_offsets[E] by thread 0: read it there only after a barrier),
+// the touched-expert list (ascending, its length in touched[E]; touched may
+// be null) and up to two grouped-GEMM schedules (a null sched skips one),
+// with a single four-way scan.  The caller has a barrier between writing
+// s_cnt and this call.
+__device__ int scan_counts_and_schedules(const int* s_cnt, int* s_offsets, int E, int32_t* __restrict__ touched,
+                                         SchedRequest s0, SchedRequest s1, int* s_work, int* s_tmp) {
   const int tid = threadIdx.x;
   int* s_tiles0 = s_work;
   int* s_tiles1 = s_work + (kMaxExperts + 1);
   int* s_base0 = s_work + 2 * (kMaxExperts + 1);
   int* s_base1 = s_work + 3 * (kMaxExperts + 1);
   int* s_tpos = s_work + 4 * (kMaxExperts + 1);
+  int* s_c = s_work + 5 * (kMaxExperts + 1);
   for (int e = tid; e < E; e += 1024) {
-    const int c = s_offsets[e + 1] - s_offsets[e];
+    const int c = s_cnt[e];
     const int m0 = s0.sched != nullptr ? (c + s0.rows_per_tile - 1) / s0.rows_per_tile : 0;
     const int m1 = s1.sched != nullptr ? (c + s1.rows_per_tile - 1) / s1.rows_per_tile : 0;
+    s_c[e] = c;
+    s_offsets[e] = c;
     s_tiles0[e] = m0;
     s_base0[e] = m0 * s0.ntiles;
     s_tiles1[e] = m1;
@@ -165,21 +178,25 @@ __device__ void build_touched_and_schedules(const int* s_offsets, int E, int32_t
     s_tpos[e] = c > 0 ? 1 : 0;
   }
   __syncthreads();
-  int* const arrays[3] = {s_base0, s_base1, s_tpos};
-  int total[3];
-  block_exclusive_scan_n<3>(arrays, E, s_tmp, total);
+  int* const arrays[4] = {s_offsets, s_base0, s_base1, s_tpos};
+  int total[4];
+  block_exclusive_scan_n<4>(arrays, E, s_tmp, total);
+  if (tid == 0) s_offsets[E] = total[0];
   if (touched != nullptr) {
-    if (tid < E && s_offsets[tid + 1] > s_offsets[tid]) touched[s_tpos[tid]] = tid;
-    if (tid == 0) touched[E] = total[2];
+    if (tid < E && s_c[tid] > 0) touched[s_tpos[tid]] = tid;
+    if (tid == 0) touched[E] = total[3];
   }
-  if (s0.sched != nullptr) {
-    if (tid == 0) s0.sched->total = total[0];
-    write_schedule_items(s_offsets, E, s0, s_tiles0, s_base0, total[0]);
+  if (tid == 0) {
+    if (s0.sched != nullptr) s0.sched->total = total[1];
+    if (s1.sched != nullptr) s1.sched->total = total[2];
   }
-  if (s1.sched != nullptr) {
-    if (tid == 0) s1.sched->total = total[1];
-    write_schedule_items(s_offsets, E, s1, s_tiles1, s_base1, total[1]);
+  // both schedules' items in one pass (totals of a null schedule are 0)
+  for (int idx = tid; idx < total[1] + total[2]; idx += 1024) {
+    const bool first = idx < total[1];
+    write_schedule_item(s_offsets, E, total[0], first ? s0 : s1, first ? s_tiles0 : s_tiles1,
+                        first ? s_base0 : s_base1, first ? idx : idx - total[1]);
   }
+  return total[0];
 }
 
 __global__ __launch_bounds__(1024) void scan_kernel(
@@ -189,7 +206,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   __shared__ int s_part[4][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
-  __shared__ int s_tmp[1024];
+  __shared__ int s_tmp[4];   // the scans' totals
   const int tid = threadIdx.x;
   const int e = tid & 255;
   const int part = tid >> 8;
@@ -214,10 +231,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     counts[tid] = c;
   }
   __syncthreads();
-  int total = block_exclusive_scan(s_offsets, E, s_tmp);
-  if (tid == 0) s_offsets[E] = total;
-  __syncthreads();
-  for (int i = tid; i <= E; i += 1024) offsets[i] = s_offsets[i];
+  const int total = scan_counts_and_schedules(s_offsets, s_offsets, E, touched, s0, s1, s_work, s_tmp);
+  for (int i = tid; i <= E; i += 1024) offsets[i] = i < E ? s_offsets[i] : total;
   // per-chunk bases
   if (e < E) {
     int run = s_offsets[e];
@@ -234,7 +249,6 @@ __global__ __launch_bounds__(1024) void scan_kernel(
         }
     }
   }
-  build_touched_and_schedules(s_offsets, E, touched, s0, s1, s_work, s_tmp);
 }
 
 // All of the above in one workgroup when the pairs fit one chunk (P <= 1024,
@@ -249,10 +263,11 @@ __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ co
   __shared__ int s_wcount[16][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
-  __shared__ int s_tmp[1024];
+  __shared__ int s_tmp[4];   // the scans' totals
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int x = tid; x < E; x += 1024) s_cnt[x] = 0;
-  for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
+  // per-wave counts of the waves that hold pairs (the others are never read)
+  for (int x = tid; x < ((P + 63) >> 6) * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
   __syncthreads();
   if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
   const int rank = wave_rank_same(e, lane);
@@ -261,15 +276,9 @@ __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ co
     atomicAdd(&s_wcount[wave][e], 1);
   }
   __syncthreads();
-  if (tid < E) {
-    s_offsets[tid] = s_cnt[tid];
-    counts[tid] = s_cnt[tid];
-  }
-  __syncthreads();
-  const int total = block_exclusive_scan(s_offsets, E, s_tmp);
-  if (tid == 0) s_offsets[E] = total;
-  __syncthreads();
-  for (int x = tid; x <= E; x += 1024) offsets[x] = s_offsets[x];
+  if (tid < E) counts[tid] = s_cnt[tid];
+  const int total = scan_counts_and_schedules(s_cnt, s_offsets, E, touched, s0, s1, s_work, s_tmp);
+  for (int x = tid; x <= E; x += 1024) offsets[x] = x < E ? s_offsets[x] : total;
   if (e >= 0) {
     int row = s_offsets[e] + rank;
     for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
@@ -278,7 +287,6 @@ __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ co
   } else if (tid < P) {
     inv[tid] = -1;   // a pair with an out-of-range id has no row
   }
-  build_touched_and_schedules(s_offsets, E, touched, s0, s1, s_work, s_tmp);
 }
 
 __global__ __launch_bounds__(1024) void permute_small_kernel(
@@ -315,12 +323,14 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         SchedRequest rq) {
+  // (offsets as moe_permute writes them: offsets[0] = 0)
+  __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
-  __shared__ int s_tmp[1024];
-  for (int i = threadIdx.x; i <= E; i += 1024) s_offsets[i] = offsets[i];
+  __shared__ int s_tmp[4];   // the scans' totals
+  for (int i = threadIdx.x; i < E; i += 1024) s_cnt[i] = offsets[i + 1] - offsets[i];
   __syncthreads();
-  build_touched_and_schedules(s_offsets, E, nullptr, rq, SchedRequest{}, s_work, s_tmp);
+  scan_counts_and_schedules(s_cnt, s_offsets, E, nullptr, rq, SchedRequest{}, s_work, s_tmp);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,

@@ -105,32 +105,36 @@ __device__ __forceinline__ void select_topk(float (&key)[4], bool (&taken)[4], i
 
 // Keys of token `tok` for a wave (lane l: experts l, l+64, l+128, l+192):
 // the slices' partial logits part[slice][T][E] added in ascending slice
-// order (the loads of 8 slices are issued together so that their latencies
-// overlap), plus the bias; experts past E are taken already and NaN keys
-// rank as -inf.
+// order, plus the bias; experts past E are taken already and NaN keys rank
+// as -inf.  The loads of 8 slices and the bias are issued together, without
+// branches (indices clamped into range, the extra values then ignored), so
+// that their latencies overlap.
 __device__ __forceinline__ void token_keys(const float* __restrict__ part, int slices, int64_t T, int64_t tok, int E,
                                            const float* __restrict__ bias, int lane, float (&key)[4],
                                            bool (&taken)[4]) {
-  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  float z[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bias != nullptr)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = bias[min(lane + 64 * q, E - 1)];
   for (int sl0 = 0; sl0 < slices; sl0 += 8) {
     float v[4][8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
+      const int ec = min(lane + 64 * q, E - 1);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[q][u] = (e < E && sl0 + u < slices) ? part[((int64_t)(sl0 + u) * T + tok) * E + e] : 0.f;
+      for (int u = 0; u < 8; ++u) v[q][u] = part[((int64_t)min(sl0 + u, slices - 1) * T + tok) * E + ec];
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) z[q] += v[q][u];
+      for (int u = 0; u < 8; ++u)
+        if (sl0 + u < slices) z[q] += v[q][u];
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     taken[q] = !(e < E);
-    key[q] = e < E ? nan_to_neg_inf(z[q] + (bias ? bias[e] : 0.f)) : -INFINITY;
+    key[q] = e < E ? nan_to_neg_inf(z[q] + b[q]) : -INFINITY;
   }
 }
 
