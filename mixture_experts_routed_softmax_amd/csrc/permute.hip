@@ -88,16 +88,20 @@ __device__ void block_exclusive_scan_n(int* const (&v)[N], int n, int* tmp, int 
 }
 
 // Rank of this lane's id among the earlier lanes of its wave holding the same
-// id: one round per distinct id in the wave (a wave of decode-sized batches
-// holds few).
-__device__ __forceinline__ int wave_rank_same(int e, int lane) {
+// id, and (n_same) how many lanes of the wave hold it: one round per distinct
+// id in the wave (a wave of decode-sized batches holds few).
+__device__ __forceinline__ int wave_rank_same(int e, int lane, int& n_same) {
   int rank = 0;
+  n_same = 0;
   uint64_t todo = ~0ull;
   while (todo != 0) {
     const int leader = __builtin_ctzll(todo);
     const int el = __builtin_amdgcn_readlane(e, leader);
     const uint64_t same = __ballot(e == el);
-    if (e == el) rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (e == el) {
+      rank = __popcll(same & ((1ull << lane) - 1ull));
+      n_same = __popcll(same);
+    }
     todo &= ~same;
   }
   return rank;
@@ -149,15 +153,35 @@ __device__ void write_schedule_item(const int* s_offsets, int E, int rows_total,
 // LDS scratch of scan_counts_and_schedules, in ints
 constexpr int kSchedWork = 6 * (kMaxExperts + 1);
 
-// From the expert counts s_cnt[0..E) (LDS, may be s_offsets itself): the
-// exclusive offsets in s_offsets[0..E) and their total (the row count, also
-// stored at s_offsets[E] by thread 0: read it there only after a barrier),
-// the touched-expert list (ascending, its length in touched[E]; touched may
-// be null) and up to two grouped-GEMM schedules (a null sched skips one),
-// with a single four-way scan.  The caller has a barrier between writing
-// s_cnt and this call.
-__device__ int scan_counts_and_schedules(const int* s_cnt, int* s_offsets, int E, int32_t* __restrict__ touched,
-                                         SchedRequest s0, SchedRequest s1, int* s_work, int* s_tmp) {
+// Sources of the expert counts for scan_counts_and_schedules
+struct CountsInLds {      // s[e] (may be the offsets array itself)
+  const int* s;
+  __device__ int operator()(int e) const { return s[e]; }
+};
+struct CountsOfWaves {    // sum of the per-wave counts w[0..nw)[e]
+  const int (*w)[kMaxExperts];
+  int nw;
+  __device__ int operator()(int e) const {
+    int c = 0;
+    for (int i = 0; i < nw; ++i) c += w[i][e];
+    return c;
+  }
+};
+struct CountsOfOffsets {  // differences of global offsets
+  const int32_t* o;
+  __device__ int operator()(int e) const { return o[e + 1] - o[e]; }
+};
+
+// From the expert counts count_of(e), e < E (written, if in LDS, before a
+// barrier): the counts in counts_out (if not null), the exclusive offsets in
+// s_offsets[0..E) and their total (the row count, also stored at s_offsets[E]
+// by thread 0: read it there only after a barrier), the touched-expert list
+// (ascending, its length in touched[E]; touched may be null) and up to two
+// grouped-GEMM schedules (a null sched skips one), with a single four-way scan.
+template <class CountOf>
+__device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__ counts_out, int* s_offsets, int E,
+                                         int32_t* __restrict__ touched, SchedRequest s0, SchedRequest s1,
+                                         int* s_work, int* s_tmp) {
   const int tid = threadIdx.x;
   int* s_tiles0 = s_work;
   int* s_tiles1 = s_work + (kMaxExperts + 1);
@@ -166,7 +190,8 @@ __device__ int scan_counts_and_schedules(const int* s_cnt, int* s_offsets, int E
   int* s_tpos = s_work + 4 * (kMaxExperts + 1);
   int* s_c = s_work + 5 * (kMaxExperts + 1);
   for (int e = tid; e < E; e += 1024) {
-    const int c = s_cnt[e];
+    const int c = count_of(e);
+    if (counts_out != nullptr) counts_out[e] = c;
     const int m0 = s0.sched != nullptr ? (c + s0.rows_per_tile - 1) / s0.rows_per_tile : 0;
     const int m1 = s1.sched != nullptr ? (c + s1.rows_per_tile - 1) / s1.rows_per_tile : 0;
     s_c[e] = c;
@@ -231,7 +256,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     counts[tid] = c;
   }
   __syncthreads();
-  const int total = scan_counts_and_schedules(s_offsets, s_offsets, E, touched, s0, s1, s_work, s_tmp);
+  const int total =
+      scan_counts_and_schedules(CountsInLds{s_offsets}, nullptr, s_offsets, E, touched, s0, s1, s_work, s_tmp);
   for (int i = tid; i <= E; i += 1024) offsets[i] = i < E ? s_offsets[i] : total;
   // per-chunk bases
   if (e < E) {
@@ -259,25 +285,22 @@ __global__ __launch_bounds__(1024) void scan_kernel(
 __device__ void permute_small_body(int e, int P, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                    int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                    int32_t* __restrict__ touched, SchedRequest s0, SchedRequest s1) {
-  __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_wcount[16][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
   __shared__ int s_tmp[4];   // the scans' totals
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int x = tid; x < E; x += 1024) s_cnt[x] = 0;
   // per-wave counts of the waves that hold pairs (the others are never read)
-  for (int x = tid; x < ((P + 63) >> 6) * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
+  const int nw = (P + 63) >> 6;
+  for (int x = tid; x < nw * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
   __syncthreads();
   if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
-  const int rank = wave_rank_same(e, lane);
-  if (e >= 0) {
-    atomicAdd(&s_cnt[e], 1);
-    atomicAdd(&s_wcount[wave][e], 1);
-  }
+  int n_same;
+  const int rank = wave_rank_same(e, lane, n_same);
+  if (e >= 0 && rank == n_same - 1) s_wcount[wave][e] = n_same;   // the wave's last lane with this id
   __syncthreads();
-  if (tid < E) counts[tid] = s_cnt[tid];
-  const int total = scan_counts_and_schedules(s_cnt, s_offsets, E, touched, s0, s1, s_work, s_tmp);
+  const int total = scan_counts_and_schedules(CountsOfWaves{s_wcount, nw}, counts, s_offsets, E, touched, s0, s1,
+                                              s_work, s_tmp);
   for (int x = tid; x <= E; x += 1024) offsets[x] = x < E ? s_offsets[x] : total;
   if (e >= 0) {
     int row = s_offsets[e] + rank;
@@ -324,13 +347,11 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         SchedRequest rq) {
   // (offsets as moe_permute writes them: offsets[0] = 0)
-  __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
   __shared__ int s_tmp[4];   // the scans' totals
-  for (int i = threadIdx.x; i < E; i += 1024) s_cnt[i] = offsets[i + 1] - offsets[i];
-  __syncthreads();
-  scan_counts_and_schedules(s_cnt, s_offsets, E, nullptr, rq, SchedRequest{}, s_work, s_tmp);
+  scan_counts_and_schedules(CountsOfOffsets{offsets}, nullptr, s_offsets, E, nullptr, rq, SchedRequest{}, s_work,
+                            s_tmp);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
@@ -359,8 +380,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     int e = ids_r[round];
     if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
     const bool valid = e >= 0;
-    const int rank = wave_rank_same(e, lane);
-    if (valid) atomicAdd(&s_wcount[wave][e], 1);
+    int n_same;
+    const int rank = wave_rank_same(e, lane, n_same);
+    if (valid && rank == n_same - 1) s_wcount[wave][e] = n_same;   // the wave's last lane with this id
     __syncthreads();
     if (valid) {
       int row = s_cursor[e] + rank;
