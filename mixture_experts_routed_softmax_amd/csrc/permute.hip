@@ -354,50 +354,35 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
                             s_tmp);
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
-                                                      int E, const int32_t* __restrict__ block_base,
-                                                      int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ inv) {
+// One workgroup of 1024 threads per chunk of 1024 pairs (one pair each): the
+// rank among the wave's earlier lanes with the same id, the wave's count of
+// each id (written by its last lane with that id), then the row: the
+// chunk's base for the expert + the earlier waves' counts + the rank.
+__global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                       int E, const int32_t* __restrict__ block_base,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ inv) {
+  static_assert(kPermChunk == 1024, "one pair per thread");
   __shared__ int s_cursor[kMaxExperts];
-  __shared__ int s_wcount[4][kMaxExperts];
+  __shared__ int s_wcount[16][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t base = (int64_t)blockIdx.x * kPermChunk;
-  // every round's ids are loaded first, together with the chunk's bases
-  int ids_r[kPermChunk / 256];
-#pragma unroll
-  for (int round = 0; round < kPermChunk / 256; ++round) {
-    const int64_t p = base + round * 256 + tid;
-    ids_r[round] = p < P ? ids[p] : -1;
-  }
-  for (int e = tid; e < E; e += 256) {
-    s_cursor[e] = block_base[(int64_t)blockIdx.x * E + e];
-    s_wcount[0][e] = s_wcount[1][e] = s_wcount[2][e] = s_wcount[3][e] = 0;
-  }
+  const int64_t p = (int64_t)blockIdx.x * kPermChunk + tid;
+  int e = p < P ? ids[p] : -1;
+  for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
+  for (int x = tid; x < E; x += 1024) s_cursor[x] = block_base[(int64_t)blockIdx.x * E + x];
   __syncthreads();
-#pragma unroll
-  for (int round = 0; round < kPermChunk / 256; ++round) {
-    const int64_t p = base + round * 256 + tid;
-    int e = ids_r[round];
-    if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
-    const bool valid = e >= 0;
-    int n_same;
-    const int rank = wave_rank_same(e, lane, n_same);
-    if (valid && rank == n_same - 1) s_wcount[wave][e] = n_same;   // the wave's last lane with this id
-    __syncthreads();
-    if (valid) {
-      int row = s_cursor[e] + rank;
-      for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
-      perm[row] = (int32_t)p;
-      inv[p] = row;
-    } else if (p < P) {
-      inv[p] = -1;   // a pair with an out-of-range id has no row
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += 256) {
-      s_cursor[x] += s_wcount[0][x] + s_wcount[1][x] + s_wcount[2][x] + s_wcount[3][x];
-      s_wcount[0][x] = s_wcount[1][x] = s_wcount[2][x] = s_wcount[3][x] = 0;
-    }
-    __syncthreads();
+  if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
+  int n_same;
+  const int rank = wave_rank_same(e, lane, n_same);
+  if (e >= 0 && rank == n_same - 1) s_wcount[wave][e] = n_same;   // the wave's last lane with this id
+  __syncthreads();
+  if (e >= 0) {
+    int row = s_cursor[e] + rank;
+    for (int w = 0; w < wave; ++w) row += s_wcount[w][e];
+    perm[row] = (int32_t)p;
+    inv[p] = row;
+  } else if (p < P) {
+    inv[p] = -1;   // a pair with an out-of-range id has no row
   }
 }
 
@@ -467,7 +452,7 @@ hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* b
                           int32_t* perm, int32_t* inv, hipStream_t stream) {
   int64_t nb = perm_blocks(P);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(256), 0, stream, ids, P, E,
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, ids, P, E,
                      block_base, perm, inv);
   return hipGetLastError();
 }
