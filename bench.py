@@ -384,7 +384,7 @@ def run_layer(args, s, L, dev, steps: int, warmup: int, decode: bool):
     cnt = counts.cpu()
     del ws, wg, wu, dn, out
     return {"ms_per_step": ms_per_step, "stages": stages, "counts": cnt, "layout": layout,
-            "graph": graph is not None, "launches": sum(n for _, n in stages.values()) / min(steps, 20)
+            "graph": graph is not None, "n_stages": sum(n for _, n in stages.values()) / min(steps, 20)
             if decode else None}
 
 
@@ -405,7 +405,7 @@ def decode_record(s, m, steps: int) -> dict:
             "tokens_per_s": round(s.T / (m["ms_per_step"] / 1e3), 1), "achieved_GBs": round(gbs, 1),
             "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "touched_experts": touched,
             "alg_bytes": alg, "steps": steps, "timing": "median of %d individually timed steps, last-level "
-            "cache evicted before each" % steps, "launches_per_step": m["launches"]}
+            "cache evicted before each" % steps, "stages_per_step": m["n_stages"]}
 
 
 def main():
@@ -506,9 +506,9 @@ def main():
             del Ld
             torch.cuda.empty_cache()
             r = decode_record(sd, md, args.decode_steps)
-            log("decode %s T=%d: %.1f us/step, %.0f GB/s = %.1f%% of HBM (%d touched experts, %.1f launches)"
+            log("decode %s T=%d: %.1f us/step, %.0f GB/s = %.1f%% of HBM (%d touched experts, %.1f timed stages)"
                 % (sd.name, T, 1e3 * r["ms_per_step"], r["achieved_GBs"], 100 * r["frac"], r["touched_experts"],
-                   r["launches_per_step"]))
+                   r["stages_per_step"]))
             dec.append(r)
 
     cpu = None
