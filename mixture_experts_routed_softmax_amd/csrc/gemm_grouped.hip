@@ -339,24 +339,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 
   // ---- epilogue.  Lane holds token l32 of each token tile and channels
-  // (r/4)*8 + hl*4 + r%4 of each 32-row weight tile.
+  // (r/4)*8 + hl*4 + r%4 of each 32-row weight tile.  bf16 outputs go through
+  // LDS (the token ring is free now): each wave writes its values in row-major
+  // order, 16-byte chunk c of row r at chunk c ^ (r & (CH-1)) (CH chunks per
+  // row), then the workgroup stores whole rows, 16 contiguous bytes per lane,
+  // instead of 8-byte pieces of 32 different rows per store instruction.
+  if constexpr (!kOutF32) {
+    constexpr int CW = kMode == 0 ? 128 : 256;   // output channels of the tile
+    constexpr int CH = CW / 8;                   // 16-byte chunks per row
+    __syncthreads();   // every wave is done with the token ring
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = it.row_begin + j * 32 + l32;
-    if (j >= ntok || row >= it.row_end) continue;
-    if (kMode == 0) {
-      uint16_t* h = (uint16_t*)a.out + (int64_t)row * N;
-      const int ch0 = it.ntile * 128 + wave * 32;
+    for (int j = 0; j < 8; ++j) {
+      const int r = j * 32 + l32;
+      if (j >= ntok || r >= valid) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = ch0 + q * 8 + hl * 4;
-        if (ch >= N) continue;
-        float v[4];
+      for (int t = 0; t < (kMode == 0 ? 1 : 2); ++t)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c];
-        *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
-      }
-    } else {
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            v[c] = kMode == 0 ? gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c]
+                              : acc[t][j][q * 4 + c];
+          const int ch = (kMode == 0 ? wave * 32 : wave * 64 + t * 32) + q * 8 + hl * 4;
+          *(i32x2*)(smem + r * (CW * 2) + (((ch >> 3) ^ (r & (CH - 1))) << 4) + ((ch >> 2) & 1) * 8) =
+              i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+        }
+    }
+    __syncthreads();
+    const int ch_tile = it.ntile * CW;
+    for (int idx = tid; idx < valid * CH; idx += kThreads) {
+      const int r = idx / CH, c = idx % CH;
+      const int ch = ch_tile + c * 8;
+      if (ch < N)
+        *(i32x4*)((uint16_t*)a.out + (int64_t)(it.row_begin + r) * N + ch) =
+            *(const i32x4*)(smem + r * (CW * 2) + ((c ^ (r & (CH - 1))) << 4));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = it.row_begin + j * 32 + l32;
+      if (j >= ntok || row >= it.row_end) continue;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -364,13 +387,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           const int ch = it.ntile * 256 + wave * 64 + t * 32 + q * 8 + hl * 4;
           if (ch >= N) continue;
           const f32x16& y = acc[t][j];
-          if (kOutF32) {
-            *(f32x4*)((float*)a.out + (int64_t)row * N + ch) =
-                f32x4{y[q * 4 + 0], y[q * 4 + 1], y[q * 4 + 2], y[q * 4 + 3]};
-          } else {
-            *(i32x2*)((uint16_t*)a.out + (int64_t)row * N + ch) =
-                i32x2{(int)pack_bf16x2(y[q * 4 + 0], y[q * 4 + 1]), (int)pack_bf16x2(y[q * 4 + 2], y[q * 4 + 3])};
-          }
+          *(f32x4*)((float*)a.out + (int64_t)row * N + ch) =
+              f32x4{y[q * 4 + 0], y[q * 4 + 1], y[q * 4 + 2], y[q * 4 + 3]};
         }
     }
   }
