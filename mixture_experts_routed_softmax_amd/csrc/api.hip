@@ -492,6 +492,9 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
                            rowinfo == nullptr);
   else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(pairs(d), d->I))
     e = launch_gemm_grouped_bf16(a, pairs(d), 1, grid, st);
+  else if (packed(d) && d->w_dtype == MOE_DT_FP8_E4M3 && d->y_dtype == MOE_DT_BF16 &&
+           gemm_grouped_fp8_fits(pairs(d), d->I))
+    e = launch_gemm_grouped_fp8(a, pairs(d), 1, grid, st);   // (dsv3_fp8 down 2.04 against 2.20 ms packed)
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);

@@ -1,7 +1,5 @@
-// Grouped gate/up GEMM of FP8 expert MLPs on tile-packed e4m3 weights with
-// 128 x 128 block scales, one wave per SIMD.  (The kernel is written for both
-// projections; only gate/up is launched: at K = 2048 the down projection runs
-// faster on gemm_packed_kernel.)
+// Grouped gate/up and down GEMMs of FP8 expert MLPs on tile-packed e4m3
+// weights with 128 x 128 block scales, one wave per SIMD.
 //
 // "Experts backends", section "FP8 and FP4 quantized experts": the experts'
 // weights are e4m3 with one scale per 128 x 128 block (float32 or UE8M0) and
@@ -370,7 +368,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 
   // ---- epilogue.  Lane holds token l32 of each token tile and channels
-  // (r/4)*8 + hl*4 + r%4 of each 32-row weight tile.
+  // (r/4)*8 + hl*4 + r%4 of each 32-row weight tile.  The outputs go through
+  // LDS (the token ring is free now): each wave writes its values in row-major
+  // order, 16-byte chunk c of row r at chunk c ^ (r & (CH-1)) (CH chunks per
+  // row), then the workgroup stores whole rows, 16 contiguous bytes per lane.
+  constexpr int RB = kMode == 0 ? 128 : 512;   // bytes per output row of the tile (fp8 h; bf16 y)
+  constexpr int CH = RB / 16;
+  static_assert(kTok * RB <= kStages * kStage, "the output tile fits the token ring");
   if (kMode == 0) {
     // h = act(g) * u, quantized per row over the tile's 128 channels
     // (s = amax / 448; 4 waves x 32 channels)
@@ -386,44 +390,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       m = fmaxf(m, __shfl_xor(m, 32));
       if (hl == 0) s_amax[wave][j * 32 + l32] = m;
     }
-    __syncthreads();
+    __syncthreads();   // (also: every wave is done with the token ring)
     const int NG = N / 128;
-    const int ch0 = it.ntile * 128 + wave * 32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = j * 32 + l32;
-      const int row = it.row_begin + r;
-      if (j >= ntok || row >= it.row_end) continue;
+      if (j >= ntok || r >= valid) continue;
       const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
       const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-      uint8_t* h = (uint8_t*)a.out + (int64_t)row * N;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(uint32_t*)(h + ch0 + q * 8 + hl * 4) =
+      for (int q = 0; q < 4; ++q) {
+        const int ch = wave * 32 + q * 8 + hl * 4;
+        *(uint32_t*)(smem + r * RB + (((ch >> 4) ^ (r & (CH - 1))) << 4) + (ch & 15)) =
             pack_fp8x4(hv[j][q * 4 + 0] / s, hv[j][q * 4 + 1] / s, hv[j][q * 4 + 2] / s, hv[j][q * 4 + 3] / s);
-      if (wave == 0 && hl == 0) a.out_scales[(int64_t)row * NG + it.ntile] = s;
+      }
+      if (wave == 0 && hl == 0) a.out_scales[(int64_t)(it.row_begin + r) * NG + it.ntile] = s;
     }
   } else {
+    __syncthreads();   // every wave is done with the token ring
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = it.row_begin + j * 32 + l32;
-      if (j >= ntok || row >= it.row_end) continue;
+      const int r = j * 32 + l32;
+      if (j >= ntok || r >= valid) continue;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ch = it.ntile * 256 + wave * 64 + t * 32 + q * 8 + hl * 4;
-          if (ch >= N) continue;
           const f32x16& y = acc[t][j];
-          if (kOutF32) {
-            *(f32x4*)((float*)a.out + (int64_t)row * N + ch) =
-                f32x4{y[q * 4 + 0], y[q * 4 + 1], y[q * 4 + 2], y[q * 4 + 3]};
-          } else {
-            *(i32x2*)((uint16_t*)a.out + (int64_t)row * N + ch) =
-                i32x2{(int)pack_bf16x2(y[q * 4 + 0], y[q * 4 + 1]), (int)pack_bf16x2(y[q * 4 + 2], y[q * 4 + 3])};
-          }
+          const int ch = wave * 64 + t * 32 + q * 8 + hl * 4;
+          *(i32x2*)(smem + r * RB + (((ch >> 3) ^ (r & (CH - 1))) << 4) + ((ch >> 2) & 1) * 8) =
+              i32x2{(int)pack_bf16x2(y[q * 4 + 0], y[q * 4 + 1]), (int)pack_bf16x2(y[q * 4 + 2], y[q * 4 + 3])};
         }
     }
+  }
+  __syncthreads();
+  const int elt = kMode == 0 ? 1 : 2;               // output bytes per channel
+  const int64_t col0 = (int64_t)it.ntile * (RB / elt);
+  for (int idx = tid; idx < valid * CH; idx += kThreads) {
+    const int r = idx / CH, c = idx % CH;
+    const int64_t ch = col0 + c * (16 / elt);
+    if (ch < N)
+      *(i32x4*)((uint8_t*)a.out + ((int64_t)(it.row_begin + r) * N + ch) * elt) =
+          *(const i32x4*)(smem + r * RB + ((c ^ (r & (CH - 1))) << 4));
   }
 }
 
@@ -438,9 +446,10 @@ hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode
   if (!gemm_grouped_fp8_fits(act_rows, a.K)) return hipErrorInvalidValue;
   GemmArgs c = a;
   c.act_rows = act_rows;
-  if (mode != 0) return hipErrorInvalidValue;   // gate/up only
+  if (mode != 0 && c.out_f32) return hipErrorInvalidValue;   // down writes bf16 y
   dim3 g(grid), b(kThreads);
-  hipLaunchKernelGGL((gemm_grouped_fp8_kernel<0, false>), g, b, 0, stream, c);
+  if (mode == 0) hipLaunchKernelGGL((gemm_grouped_fp8_kernel<0, false>), g, b, 0, stream, c);
+  else hipLaunchKernelGGL((gemm_grouped_fp8_kernel<1, false>), g, b, 0, stream, c);
   return hipGetLastError();
 }
 

@@ -126,8 +126,7 @@ hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, int64_t act_rows, int mod
 // fp8 (e4m3, 128 x 128 block scales) grouped GEMM on packed weights with one
 // wave per SIMD, 128 token rows per tile; takes K a multiple of 128 up to
 // 128 * kStreamMaxScaleBlocks and activations spanning at most 4 GiB.
-// Gate/up only (mode 0): down stays on gemm_packed_kernel, which measured
-// faster at the DSv3-like K = 2048.
+// Mode 0 gate/up (fp8 h and its scales), mode 1 down (bf16 y only).
 bool gemm_grouped_fp8_fits(int64_t act_rows, int K);
 hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
