@@ -127,6 +127,14 @@ def test_forward_f32_intermediate_rows(layout):
     _check_forward(s, L, hl, y_dtype="f32", layout=layout)
 
 
+def test_fp8_forward_f32_intermediate_rows():
+    """fp8 experts with float32 y rows: the down projection then runs on the
+    packed fp8 kernel (the grouped fp8 kernel writes bf16 y only)."""
+    s = SMALL["fp8_f32"]
+    L, hl = _layer(s, seed=4)
+    _check_forward(s, L, hl, y_dtype="f32", layout="packed")
+
+
 @pytest.mark.parametrize("name", ["bf16_ragged", "fp8_f32"])
 def test_packed_layout_bytes(name):
     """moe_pack_weights writes the layout include/moe.h documents (checked
