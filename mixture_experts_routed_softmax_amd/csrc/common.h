@@ -52,11 +52,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // gate activation of the gated MLP (moe_gate_act: 0 silu, 1 gelu, 2 relu);
-// gelu is the exact form 0.5 g (1 + erf(g / sqrt 2)).  `act` is uniform.
+// gelu is the exact form 0.5 g (1 + erf(g / sqrt 2)).
+template <int kAct>
+__device__ __forceinline__ float gate_act(float g) {
+  if constexpr (kAct == 1) return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+  else if constexpr (kAct == 2) return fmaxf(g, 0.0f);
+  else return silu(g);
+}
+// the same with the activation chosen at run time (`act` is uniform)
 __device__ __forceinline__ float gate_fn(float g, int act) {
-  if (act == 1) return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
-  if (act == 2) return fmaxf(g, 0.0f);
-  return silu(g);
+  if (act == 1) return gate_act<1>(g);
+  if (act == 2) return gate_act<2>(g);
+  return gate_act<0>(g);
 }
 
 // Router keys: a NaN key ranks as -inf, so it loses to every number and ties

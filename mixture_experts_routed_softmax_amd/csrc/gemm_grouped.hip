@@ -348,24 +348,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int CW = kMode == 0 ? 128 : 256;   // output channels of the tile
     constexpr int CH = CW / 8;                   // 16-byte chunks per row
     __syncthreads();   // every wave is done with the token ring
+    // Every lane converts its values without conditions (rows past the item
+    // land in LDS rows that are never stored; only whole dead token tiles,
+    // a uniform condition, are skipped), with the gate activation fixed at
+    // compile time, so that the conversion is straight-line code.
+    auto stage = [&](auto act_const) {
+      constexpr int kAct = decltype(act_const)::value;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = j * 32 + l32;
-      if (j >= ntok || r >= valid) continue;
+      for (int j = 0; j < 8; ++j) {
+        if (j >= ntok) break;
+        const int r = j * 32 + l32;
 #pragma unroll
-      for (int t = 0; t < (kMode == 0 ? 1 : 2); ++t)
+        for (int t = 0; t < (kMode == 0 ? 1 : 2); ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v[4];
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            v[c] = kMode == 0 ? gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c]
-                              : acc[t][j][q * 4 + c];
-          const int ch = (kMode == 0 ? wave * 32 : wave * 64 + t * 32) + q * 8 + hl * 4;
-          *(i32x2*)(smem + r * (CW * 2) + (((ch >> 3) ^ (r & (CH - 1))) << 4) + ((ch >> 2) & 1) * 8) =
-              i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
-        }
-    }
+            for (int c = 0; c < 4; ++c)
+              v[c] = kMode == 0 ? gate_act<kAct>(acc[0][j][q * 4 + c]) * acc[1][j][q * 4 + c]
+                                : acc[t][j][q * 4 + c];
+            const int ch = (kMode == 0 ? wave * 32 : wave * 64 + t * 32) + q * 8 + hl * 4;
+            *(i32x2*)(smem + r * (CW * 2) + (((ch >> 3) ^ (r & (CH - 1))) << 4) + ((ch >> 2) & 1) * 8) =
+                i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+          }
+      }
+    };
+    if (kMode != 0 || a.gate_act == 0) stage(std::integral_constant<int, 0>{});
+    else if (a.gate_act == 1) stage(std::integral_constant<int, 1>{});
+    else stage(std::integral_constant<int, 2>{});
     __syncthreads();
     const int ch_tile = it.ntile * CW;
     for (int idx = tid; idx < valid * CH; idx += kThreads) {
