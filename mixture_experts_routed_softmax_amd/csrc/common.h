@@ -1,5 +1,6 @@
 // Device-side helpers shared by the libmoe kernels (gfx950, wave64).
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,6 +65,20 @@ __device__ __forceinline__ float gate_fn(float g, int act) {
   if (act == 1) return gate_act<1>(g);
   if (act == 2) return gate_act<2>(g);
   return gate_act<0>(g);
+}
+// Calls f(std::integral_constant<int, act>{}) for the uniform activation id,
+// so that a loop of activations inside f is straight-line code.
+template <class F>
+__device__ __forceinline__ void with_gate_act(int act, F&& f) {
+  if (act == 1) f(std::integral_constant<int, 1>{});
+  else if (act == 2) f(std::integral_constant<int, 2>{});
+  else f(std::integral_constant<int, 0>{});
+}
+// h = act(g) * u over the 16 values a lane holds of a 32 x 32 tile pair
+template <int kAct>
+__device__ __forceinline__ void gated16(const f32x16& g, const f32x16& u, float (&h)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) h[r] = gate_act<kAct>(g[r]) * u[r];
 }
 
 // Router keys: a NaN key ranks as -inf, so it loses to every number and ties

@@ -213,7 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 
   // ---- epilogue.  Lane holds token l32 of each token tile and channels
-  // (r/4)*8 + hl*4 + r%4 of each 32-row weight tile.
+  // (r/4)*8 + hl*4 + r%4 of each 32-row weight tile.  The gated activations
+  // of every live token tile come first, as straight-line code.
+  float hv[4][16];
+  if (kMode == 0 && !a.gu_out)
+    with_gate_act(a.gate_act, [&](auto k) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= ntok) break;
+        gated16<decltype(k)::value>(acc[0][j], acc[1][j], hv[j]);
+      }
+    });
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = it.row_begin + j * 32 + l32;
@@ -239,8 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
           if (ch >= N) continue;
           uint16_t v[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            v[c] = f32_to_bf16_bits(gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c]);
+          for (int c = 0; c < 4; ++c) v[c] = f32_to_bf16_bits(hv[j][q * 4 + c]);
           i32x2 pk = {(int)(v[0] | ((uint32_t)v[1] << 16)), (int)(v[2] | ((uint32_t)v[3] << 16))};
           *(i32x2*)(h + ch) = pk;
         }

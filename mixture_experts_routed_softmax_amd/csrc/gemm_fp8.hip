@@ -187,17 +187,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
   if (kMode == 0) {
     // SwiGLU, then per-row quantization over the tile's 128 channels
     float hv[2][2][16];
+    with_gate_act(a.gate_act, [&](auto k) {
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) gated16<decltype(k)::value>(acc[i][tj], acc[2 + i][tj], hv[tj][i]);
+    });
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj) {
       float m = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = gate_fn(acc[i][tj][r], a.gate_act) * acc[2 + i][tj][r];
-          hv[tj][i][r] = v;
-          m = fmaxf(m, fabsf(v));
-        }
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(hv[tj][i][r]));
       m = fmaxf(m, __shfl_xor(m, 32));
       if (lhi == 0) s_amax[wm][brow0 + 32 * tj + l32] = m;
     }

@@ -378,25 +378,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (kMode == 0) {
     // h = act(g) * u, quantized per row over the tile's 128 channels
     // (s = amax / 448; 4 waves x 32 channels)
-    // (the gate activation fixed at compile time: straight-line code)
     float hv[4][16];
-    auto act_rows = [&](auto act_const) {
-      constexpr int kAct = decltype(act_const)::value;
+    with_gate_act(a.gate_act, [&](auto k) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float m = 0.f;
+      for (int j = 0; j < 4; ++j) gated16<decltype(k)::value>(acc[0][j], acc[1][j], hv[j]);
+    });
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          hv[j][r] = gate_act<kAct>(acc[0][j][r]) * acc[1][j][r];
-          m = fmaxf(m, fabsf(hv[j][r]));
-        }
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if (hl == 0) s_amax[wave][j * 32 + l32] = m;
-      }
-    };
-    if (a.gate_act == 0) act_rows(std::integral_constant<int, 0>{});
-    else if (a.gate_act == 1) act_rows(std::integral_constant<int, 1>{});
-    else act_rows(std::integral_constant<int, 2>{});
+    for (int j = 0; j < 4; ++j) {
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(hv[j][r]));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (hl == 0) s_amax[wave][j * 32 + l32] = m;
+    }
     __syncthreads();   // (also: every wave is done with the token ring)
     const int NG = N / 128;
 #pragma unroll

@@ -468,14 +468,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
     if constexpr (kFp8) {
       __shared__ float s_amax[4][kTok];
       float hv[kNTW][16];
+      with_gate_act(a.gate_act, [&](auto k) {
+#pragma unroll
+        for (int j = 0; j < kNTW; ++j) gated16<decltype(k)::value>(acc[0][j], acc[1][j], hv[j]);
+      });
 #pragma unroll
       for (int j = 0; j < kNTW; ++j) {
         float m = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          hv[j][r] = gate_fn(acc[0][j][r], a.gate_act) * acc[1][j][r];
-          m = fmaxf(m, fabsf(hv[j][r]));
-        }
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(hv[j][r]));
         m = fmaxf(m, __shfl_xor(m, 32));
         if (hl == 0) s_amax[rg][brow + j * 32 + l32] = m;
       }
@@ -498,6 +499,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
         if (rg == 0 && hl == 0) a.out_scales[(int64_t)row * NG + it.ntile] = s;
       }
     } else {
+      // activations of every live token tile first (straight-line code),
+      // then the stores of the lane's rows
+      float hv[kNTW][16];
+      with_gate_act(a.gate_act, [&](auto k) {
+#pragma unroll
+        for (int j = 0; j < kNTW; ++j) {
+          if (j >= my_nt) break;
+          gated16<decltype(k)::value>(acc[0][j], acc[1][j], hv[j]);
+        }
+      });
 #pragma unroll
       for (int j = 0; j < kNTW; ++j) {
         const int row = it.row_begin + brow + j * 32 + l32;
@@ -507,10 +518,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs a) {
         for (int q = 0; q < 4; ++q) {
           const int ch = ch0 + q * 8 + hl * 4;
           if (ch >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c];
-          *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+          *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(hv[j][q * 4 + 0], hv[j][q * 4 + 1]),
+                                    (int)pack_bf16x2(hv[j][q * 4 + 2], hv[j][q * 4 + 3])};
         }
       }
     }

@@ -87,14 +87,15 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
     if constexpr (kFp8) {
       __shared__ float s_amax[4][64];
       float hv[NT][16];
+      with_gate_act(a.gate_act, [&](auto k) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) gated16<decltype(k)::value>(acc[0][j], acc[1][j], hv[j]);
+      });
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         float m = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          hv[j][r] = gate_fn(acc[0][j][r], a.gate_act) * acc[1][j][r];
-          m = fmaxf(m, fabsf(hv[j][r]));
-        }
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(hv[j][r]));
         m = fmaxf(m, __shfl_xor(m, 32));
         if (hl == 0) s_amax[wave][j * 32 + l32] = m;
       }
@@ -115,6 +116,11 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
         if (wave == 0 && hl == 0) a.out_scales[(int64_t)row * NG + it.ntile] = s;
       }
     } else {
+      float hv[NT][16];
+      with_gate_act(a.gate_act, [&](auto k) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) gated16<decltype(k)::value>(acc[0][j], acc[1][j], hv[j]);
+      });
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int row = it.row_begin + j * 32 + l32;
@@ -124,10 +130,8 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs& a, const WorkIte
         for (int q = 0; q < 4; ++q) {
           const int ch = ch0 + q * 8 + hl * 4;
           if (ch >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = gate_fn(acc[0][j][q * 4 + c], a.gate_act) * acc[1][j][q * 4 + c];
-          *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+          *(i32x2*)(h + ch) = i32x2{(int)pack_bf16x2(hv[j][q * 4 + 0], hv[j][q * 4 + 1]),
+                                    (int)pack_bf16x2(hv[j][q * 4 + 2], hv[j][q * 4 + 3])};
         }
       }
     }
