@@ -475,14 +475,14 @@ def main():
         flops = 2.0 * P * s.H * 2 * s.I
         achieved = flops / (avg_ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[s.experts]
-        # the gate/up kernel the library launches for this layer (packed bf16
-        # weights with H >= 4096: the one-wave-per-SIMD grouped GEMM)
-        if s.experts == "bf16" and s.H >= 4096:
+        # the gate/up kernel the library launches for this layer (packed
+        # weights: the one-wave-per-SIMD grouped GEMMs for bf16 and fp8)
+        if s.experts == "bf16":
             kname = "gemm_grouped_bf16_kernel<0, false>"
         elif s.experts == "fp8":
             kname = "gemm_grouped_fp8_kernel<0, false>"
         else:
-            kname = "gemm_packed_kernel<%d, 0, false>" % {"fp4": 2}.get(s.experts, 0)   # bf16 below H = 4096 too
+            kname = "gemm_packed_kernel<2, 0, false>"
         traffic = recorded_traffic(s.name, kname) if layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),

@@ -163,12 +163,10 @@ size_t packed_bytes(const moe_desc* d, int which) {
   return (size_t)d->E * tiles * 256 * w_row_bytes(d->w_dtype, K);
 }
 
-// bf16 gate/up on packed weights takes the one-wave-per-SIMD grouped kernel
-// from this reduction length on, gemm_packed_kernel below it (kernel traces,
-// grouped against packed: H = 7168 4.50 vs 4.70 ms, H = 2048 299 vs 276-284
-// us).  Down always takes the grouped kernel (I = 2048 2.60 vs 2.71 ms,
-// I = 1408 157 vs 158-162 us).
-constexpr int kGroupedGateUpMinK = 4096;
+// bf16 gate/up and down on packed weights take the one-wave-per-SIMD grouped
+// kernel (kernel traces against gemm_packed_kernel: gate/up H = 7168 4.27 vs
+// 4.70 ms, H = 2048 260-263 vs 281-287 us; down I = 2048 2.48 vs 2.71 ms,
+// I = 1408 154-158 vs 158-162 us)
 
 // prefill schedules: an expert's items in blocks of kSchedBlockM row tiles x
 // kSchedBlockN channel tiles, one block per XCD chunk of the grouped GEMMs
@@ -451,8 +449,7 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
   if (use_stream(d))
     e = launch_gemm_stream(a, wfmt(d), 0, grid_for(stream_units_cap(sched_capacity(d, gate_up_ntiles(d)))),
                            (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), d->T <= 32, st);
-  else if (packed(d) && d->w_dtype == MOE_DT_BF16 && d->H >= kGroupedGateUpMinK &&
-           gemm_grouped_bf16_fits(act_rows, d->H))
+  else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(act_rows, d->H))
     e = launch_gemm_grouped_bf16(a, act_rows, 0, grid, st);
   else if (packed(d) && d->w_dtype == MOE_DT_FP8_E4M3 && gemm_grouped_fp8_fits(act_rows, d->H))
     e = launch_gemm_grouped_fp8(a, act_rows, 0, grid, st);   // (measured faster than the packed kernel for gate/up only)

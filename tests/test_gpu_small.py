@@ -26,8 +26,7 @@ SMALL = {
     "fp8_f32": synthetic.spec("dsv3_fp8", T=100, H=256, I=384, E=16, k=4),
     "fp8_ue8m0": synthetic.spec("dsv3_fp8", T=100, H=256, I=384, E=16, k=4, scale_fmt="ue8m0"),
     "fp4": synthetic.spec("dsv3_fp4", T=100, H=256, I=384, E=16, k=4),
-    # a reduction length at which bf16 gate/up on packed weights takes the
-    # one-wave-per-SIMD grouped kernel
+    # a long reduction (64 K steps of the grouped kernel's pipeline)
     "bf16_long_k": synthetic.spec("dsv3_bf16", T=96, H=4096, I=512, E=8, k=2),
 }
 
