@@ -301,7 +301,40 @@ __global__ __launch_bounds__(kBwdThreads, 1) void gemm_bwd_kernel(BwdGemmArgs a)
   }
 
   // ---- epilogue: lane holds C[m][n] for n = l32 of each B tile and
-  // m = (r/4)*8 + hl*4 + r%4 of each A tile; out[n][m], 4 consecutive m per store
+  // m = (r/4)*8 + hl*4 + r%4 of each A tile; out[n][m].
+  if (kRK && !a.out_f32) {
+    // bf16 weight gradients go through LDS (the ring is free now): each wave
+    // writes its values in out[n][m] order, 16-byte chunk c of tile row r at
+    // chunk c ^ (r & 31), then the workgroup stores whole rows, 16 contiguous
+    // bytes per lane, instead of 8-byte pieces of 32 rows per store.
+    static_assert(kTile * kTile * 2 <= kStagesB * kStageB, "the bf16 tile fits the ring");
+    __syncthreads();   // every wave is done with the ring
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      const int r = wn * 128 + tj * 32 + l32;
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ml = wm * 64 + ti * 32 + q * 8 + hl * 4;
+          const f32x16& c = acc[ti][tj];
+          *(i32x2*)(smem + r * (kTile * 2) + (((ml >> 3) ^ (r & 31)) << 4) + ((ml >> 2) & 1) * 8) =
+              i32x2{(int)pack_bf16x2(c[q * 4 + 0], c[q * 4 + 1]), (int)pack_bf16x2(c[q * 4 + 2], c[q * 4 + 3])};
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kTile * (kTile / 8); idx += kBwdThreads) {
+      const int r = idx / (kTile / 8), c = idx % (kTile / 8);
+      const int n = nt * kTile + r, m = mt * kTile + c * 8;
+      if (n >= a.n_valid || m >= a.M) continue;
+      const bool second = a.out2 && n >= a.n_split;
+      const int nn = second ? n - a.n_split : n;
+      uint8_t* base = (uint8_t*)(second ? a.out2 : a.out);
+      *(i32x4*)(base + ((int64_t)e * a.o_gs + (int64_t)nn * a.ldo + m) * 2) =
+          *(const i32x4*)(smem + r * (kTile * 2) + ((c ^ (r & 31)) << 4));
+    }
+    return;
+  }
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
     const int rr = wn * 128 + tj * 32 + l32;
