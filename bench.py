@@ -476,13 +476,10 @@ def main():
         achieved = flops / (avg_ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[s.experts]
         # the gate/up kernel the library launches for this layer (packed
-        # weights: the one-wave-per-SIMD grouped GEMMs for bf16 and fp8)
-        if s.experts == "bf16":
-            kname = "gemm_grouped_bf16_kernel<0, false>"
-        elif s.experts == "fp8":
-            kname = "gemm_grouped_fp8_kernel<0, false>"
-        else:
-            kname = "gemm_packed_kernel<2, 0, false>"
+        # weights: the one-wave-per-SIMD grouped GEMMs; fp8 and fp4 weights
+        # share the e4m3-activation one)
+        kname = {"bf16": "gemm_grouped_bf16_kernel<0, false>", "fp8": "gemm_grouped_fp8_kernel<0, false>",
+                 "fp4": "gemm_grouped_fp8_kernel<0, true>"}.get(s.experts, "")
         traffic = recorded_traffic(s.name, kname) if layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),

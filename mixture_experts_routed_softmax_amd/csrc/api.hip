@@ -166,7 +166,9 @@ size_t packed_bytes(const moe_desc* d, int which) {
 // bf16 gate/up and down on packed weights take the one-wave-per-SIMD grouped
 // kernel (kernel traces against gemm_packed_kernel: gate/up H = 7168 4.27 vs
 // 4.70 ms, H = 2048 260-263 vs 281-287 us; down I = 2048 2.48 vs 2.71 ms,
-// I = 1408 154-158 vs 158-162 us)
+// I = 1408 154-158 vs 158-162 us); fp8 and fp4 experts the e4m3 one (fp8
+// gate/up 3.08 vs 4.17 ms, down 2.04 vs 2.20 ms; fp4 gate/up 2.80 vs
+// 3.65 ms, down 1.90 vs 2.08 ms)
 
 // prefill schedules: an expert's items in blocks of kSchedBlockM row tiles x
 // kSchedBlockN channel tiles, one block per XCD chunk of the grouped GEMMs
@@ -451,8 +453,8 @@ moe_status run_gate_up(const moe_desc* d, const void* act, const float* act_scal
                            (int)std::min<int64_t>(sched_capacity(d, gate_up_ntiles(d)), kStreamTarget), d->T <= 32, st);
   else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(act_rows, d->H))
     e = launch_gemm_grouped_bf16(a, act_rows, 0, grid, st);
-  else if (packed(d) && d->w_dtype == MOE_DT_FP8_E4M3 && gemm_grouped_fp8_fits(act_rows, d->H))
-    e = launch_gemm_grouped_fp8(a, act_rows, 0, grid, st);   // (measured faster than the packed kernel for gate/up only)
+  else if (packed(d) && is_fp8(d) && gemm_grouped_fp8_fits(act_rows, d->H))
+    e = launch_gemm_grouped_fp8(a, act_rows, 0, d->w_dtype == MOE_DT_FP4_E2M1, grid, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 0, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_gate_up_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_gate_up_bf16(a, grid, st);
@@ -489,9 +491,8 @@ moe_status run_down(const moe_desc* d, const void* h, const float* hs, const int
                            rowinfo == nullptr);
   else if (packed(d) && d->w_dtype == MOE_DT_BF16 && gemm_grouped_bf16_fits(pairs(d), d->I))
     e = launch_gemm_grouped_bf16(a, pairs(d), 1, grid, st);
-  else if (packed(d) && d->w_dtype == MOE_DT_FP8_E4M3 && d->y_dtype == MOE_DT_BF16 &&
-           gemm_grouped_fp8_fits(pairs(d), d->I))
-    e = launch_gemm_grouped_fp8(a, pairs(d), 1, grid, st);   // (dsv3_fp8 down 2.04 against 2.20 ms packed)
+  else if (packed(d) && is_fp8(d) && d->y_dtype == MOE_DT_BF16 && gemm_grouped_fp8_fits(pairs(d), d->I))
+    e = launch_gemm_grouped_fp8(a, pairs(d), 1, d->w_dtype == MOE_DT_FP4_E2M1, grid, st);
   else if (packed(d)) e = launch_gemm_packed(a, wfmt(d), 1, grid, st);
   else if (d->w_dtype == MOE_DT_F32) e = launch_down_f32(a, st);
   else if (d->w_dtype == MOE_DT_BF16) e = launch_down_bf16(a, grid, st);

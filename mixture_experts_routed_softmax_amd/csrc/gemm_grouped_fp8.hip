@@ -29,6 +29,15 @@
 // cache line, one scale block) per row and block.  One barrier per block.
 // The scales of the whole K range (the tile's rows' activation scales and
 // the weight blocks' scales) are staged in LDS once per tile.
+//
+// FP4 experts (same section: e2m1 weights, two per byte, one UE8M0 scale per
+// row and 32 consecutive K) run on the same kernel (kFp4): a 128-deep block is
+// then 64 packed bytes per weight row, one 16 KB chunk, and the MFMA takes
+// the e2m1 weights as its A operand (a lane half holds 32 consecutive K, the
+// matching e4m3 token bytes are the same pieces as for fp8 weights) with the
+// lane's weight scale byte as its scale operand, so the promotion multiplies
+// by s_x(row, block) alone.  The scale dword of a weight row (the block's four
+// 32-K scales) rides with the block's weight loads.
 #include <type_traits>
 
 #include "common.h"
@@ -47,7 +56,10 @@ constexpr int kTokAhead = kStages - 1;   // blocks the token DMA runs ahead
 constexpr int kWSlots = 3;               // register slots of weights (blocks)
 constexpr int kWAhead = kWSlots - 1;     // blocks the weight loads run ahead
 constexpr int kChunk = 256 * 64;         // packed weight chunk: 256 rows x 64 bytes (64 K)
-constexpr int kWLoads = 8;               // weight loads per wave and block
+// weight loads per wave and block: fp8 8 x 16 bytes; fp4 4 x 16 bytes and
+// the two weight tiles' scale dwords
+template <bool kFp4>
+constexpr int kWLoads = kFp4 ? 6 : 8;
 constexpr int kMaxKB = kStreamMaxScaleBlocks;   // K / 128 at most (K <= 8192)
 static_assert(kThreads == 2 * kTok, "two threads stage each token row's scales");
 // word 3 of a gfx9 buffer resource: 32-bit data format, raw (untyped) access
@@ -85,18 +97,23 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   }
 }
 
-// weights of one block for one wave: [weight tile][64-deep half][16-byte piece]
+// weights of one block for one wave: [weight tile][64-deep half][16-byte
+// piece] (fp4: one piece per half, and the tiles' scale dwords)
+template <bool kFp4>
 struct WBlk {
-  i32x4 a[2][2][2];
+  i32x4 a[2][2][kFp4 ? 1 : 2];
+  uint32_t s[kFp4 ? 2 : 1];
 };
 
 __device__ __forceinline__ i32x8 join8(const i32x4& lo, const i32x4& hi) {
   return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-template <int kMode, bool kOutF32>
+template <int kMode, bool kFp4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_fp8_kernel(
     GemmArgs a) {
+  constexpr int kWL = kWLoads<kFp4>;
+  constexpr int kBlkW = kFp4 ? kChunk : 2 * kChunk;   // packed weight bytes of a 128-deep block
   // one LDS object: the token ring, then the activation scales of the tile's
   // rows [kb][row], the weight block scales (gate/up: gate, up; down: row
   // halves) and the gate/up epilogue's per-wave row maxima of |h|
@@ -118,9 +135,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // ---- weights: a buffer resource over the tile's packed chunks; the lane's
   // pieces at fixed offsets, the K step as scalar offset
-  const uint8_t* wbase = (const uint8_t*)a.w0 + ((int64_t)e * a.wtiles + it.ntile) * (2 * KB) * (int64_t)kChunk;
-  const __amdgpu_buffer_rsrc_t wres =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, 2 * KB * kChunk, kBufferConfig);
+  const uint8_t* wbase = (const uint8_t*)a.w0 + ((int64_t)e * a.wtiles + it.ntile) * KB * (int64_t)kBlkW;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, KB * kBlkW, kBufferConfig);
   int arow[2];
   if (kMode == 0) {
     arow[0] = wave * 32 + l32;          // gate rows of channels wave*32 .. +31
@@ -133,20 +149,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // free as long as the weights and the tokens agree (the MFMA sums over all
   // 64): lane half hl takes the 16-byte pieces hl and hl + 2 of a 64-byte K
   // step, so that the two lane halves' token reads hit different LDS banks.
+  // (fp4: the e2m1 operand of lane half hl in 64-deep half q is the 16-byte
+  // piece 2q + hl, i.e. 32 consecutive K, of the block's 64-byte row; paired
+  // with the same token pieces as for fp8 weights, as the MFMA lays the two
+  // formats out)
   int aoff[2][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int q = 0; q < 2; ++q) aoff[t][q] = wswz(arow[t], 2 * q + hl);
-  auto load_w = [&](WBlk& wb, int kb) {
+  // fp4 weight scales: K / 32 UE8M0 bytes per weight row (gate/up: gate rows
+  // in s0, up rows in s1), the block's four in one dword; rows past N take
+  // the last row's scales (their packed weights are zero)
+  __amdgpu_buffer_rsrc_t sres[2];
+  int soff[2];
+  if constexpr (kFp4) {
+    const int KS = K / 32;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int t = 0; t < 2; ++t) {
+      int ch = kMode == 0 ? it.ntile * 128 + (arow[t] & 127) : it.ntile * 256 + arow[t];
+      ch = ch < N ? ch : N - 1;
+      const uint8_t* sb = (const uint8_t*)(kMode == 0 && t == 1 ? a.s1 : a.s0) + (int64_t)e * N * KS;
+      sres[t] = __builtin_amdgcn_make_buffer_rsrc((void*)sb, 0, N * KS, kBufferConfig);
+      soff[t] = ch * KS;
+    }
+  }
+  auto load_w = [&](WBlk<kFp4>& wb, int kb) {
+    if constexpr (kFp4) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          wb.a[t][h][q] = __builtin_bit_cast(
-              i32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, aoff[t][q], (2 * kb + h) * kChunk, 0));
+        for (int t = 0; t < 2; ++t)
+          wb.a[t][h][0] =
+              __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, aoff[t][h], kb * kBlkW, 0));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) wb.s[t] = __builtin_amdgcn_raw_buffer_load_b32(sres[t], soff[t], kb * 4, 0);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            wb.a[t][h][q] = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, aoff[t][q], (2 * kb + h) * kChunk, 0));
+    }
+  };
+  // one MFMA of weight tile t, 64-deep half h (unit scales for fp8; fp4: the
+  // lane's 32-K weight scale byte 2h + hl of the tile row's dword)
+  auto mfma = [&](const WBlk<kFp4>& wb, int t, int h, const i32x8& b, const f32x16& c) {
+    if constexpr (kFp4) {
+      const i32x4 v = wb.a[t][h][0];
+      const int sc = (int)__builtin_amdgcn_ubfe(wb.s[t], 16 * h + 8 * hl, 8);
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}, b, c, 4, 0,
+                                                             0, sc, 0, 127);
+    } else {
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join8(wb.a[t][h][0], wb.a[t][h][1]), b, c, 0, 0, 0,
+                                                             127, 0, 127);
+    }
   };
 
   // ---- tokens: DMA instruction i of wave w fills LDS rows 32i + 8w .. +8 of
@@ -166,7 +226,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // ---- scales of the whole K range into LDS: the activation scales of the
   // tile's rows as s_sx[kb][row] (two threads per row, every load issued
-  // before the first store) and the weight blocks' scales
+  // before the first store) and the fp8 weight blocks' scales
   {
     const int row = tid >> 1, half = tid & 1;
     int r = it.row_begin + row;
@@ -185,7 +245,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (kb < KB) s_sx[kb * kTok + row] = v[u];
     }
     const int NBr = (N + 127) / 128;
-    for (int i = tid; i < 2 * KB; i += kThreads) {
+    for (int i = tid; i < (kFp4 ? 0 : 2 * KB); i += kThreads) {
       const int h = i / KB, kb = i - h * KB;
       if (kMode == 0) {
         s_sw[h][kb] = wscale(h == 0 ? a.s0 : a.s1, a.scale_ue8m0, ((int64_t)e * NBr + it.ntile) * KB + kb);
@@ -217,14 +277,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // of block t + kTokAhead, then the weights of block t + kWAhead)
     auto ops_after = [&](int j, int upto) {
       const int t0 = j - kTokAhead;
-      int n = (t0 + kWAhead >= 0 && t0 + kWAhead < KB) ? kWLoads : 0;
+      int n = (t0 + kWAhead >= 0 && t0 + kWAhead < KB) ? kWL : 0;
       for (int t = t0 + 1; t <= upto; ++t) {
         if (t + kTokAhead >= 0 && t + kTokAhead < KB) n += NT;
-        if (t + kWAhead >= 0 && t + kWAhead < KB) n += kWLoads;
+        if (t + kWAhead >= 0 && t + kWAhead < KB) n += kWL;
       }
       return n;
     };
-    WBlk ring[kWSlots];
+    WBlk<kFp4> ring[kWSlots];
     // prologue: the tops t < 0
 #pragma unroll
     for (int t = -kTokAhead; t < 0; ++t) {
@@ -252,7 +312,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // state (every earlier top issued in full, kb + kTokAhead < KB) the wait
     // is a compile-time count and the loads are issued without conditions,
     // so that the compiler's own waits for the weight registers stay exact.
-    constexpr int kSteadyWait = kWLoads + (kTokAhead - 2) * (NT + kWLoads);
+    constexpr int kSteadyWait = kWL + (kTokAhead - 2) * (NT + kWL);
     static_assert(kSteadyWait < 64, "vmcnt range");
     auto block = [&](int kb, auto d_const, auto p_const, auto steady_const) {
       constexpr int d = decltype(d_const)::value;
@@ -267,8 +327,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (kSteady || kb + kTokAhead < KB) issue_t((kb + kTokAhead) % kStages, kb + kTokAhead);
       if (kSteady || kb + kWAhead < KB) load_w(ring[df], kb + kWAhead);
       // gate/up: gate and up tiles; down: both tiles lie in row half wave >> 1
-      const float sw0 = s_sw[kMode == 0 ? 0 : (wave >> 1)][kb];
-      const float sw1 = s_sw[kMode == 0 ? 1 : (wave >> 1)][kb];
+      // (fp4: the MFMA applied the weight scales)
+      const float sw0 = kFp4 ? 1.f : s_sw[kMode == 0 ? 0 : (wave >> 1)][kb];
+      const float sw1 = kFp4 ? 1.f : s_sw[kMode == 0 ? 1 : (wave >> 1)][kb];
       float m[2][NT];   // s_w(kb) * s_x(row, kb); lane holds token l32 of each token tile
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -292,8 +353,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int sl = 0; sl < NK + 2; ++sl) {
         if (sl < NK) {
           const int j = sl >> 1, t = sl & 1;
-          part[sl] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              join8(ring[d].a[t][0][0], ring[d].a[t][0][1]), fb[p][0][j], f32x16{}, 0, 0, 0, 127, 0, 127);
+          part[sl] = mfma(ring[d], t, 0, fb[p][0][j], f32x16{});
         }
         __builtin_amdgcn_sched_barrier(0);
         if (sl >= 2) {
@@ -304,8 +364,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         __builtin_amdgcn_sched_barrier(0);
         if (sl >= 1 && sl - 1 < NK) {
           const int k = sl - 1, j = k >> 1, t = k & 1;
-          part[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              join8(ring[d].a[t][1][0], ring[d].a[t][1][1]), fb[p][1][j], part[k], 0, 0, 0, 127, 0, 127);
+          part[k] = mfma(ring[d], t, 1, fb[p][1][j], part[k]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (sl >= 2) {
@@ -442,15 +501,22 @@ bool gemm_grouped_fp8_fits(int64_t act_rows, int K) {
   return K % 128 == 0 && K / 128 <= kMaxKB && act_rows * (int64_t)K <= (int64_t)UINT32_MAX;
 }
 
-hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream) {
+hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode, bool fp4, int grid,
+                                   hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   if (!gemm_grouped_fp8_fits(act_rows, a.K)) return hipErrorInvalidValue;
   GemmArgs c = a;
   c.act_rows = act_rows;
   if (mode != 0 && c.out_f32) return hipErrorInvalidValue;   // down writes bf16 y
+  if (fp4 && !c.scale_ue8m0) return hipErrorInvalidValue;   // fp4 weights carry UE8M0 scales
   dim3 g(grid), b(kThreads);
-  if (mode == 0) hipLaunchKernelGGL((gemm_grouped_fp8_kernel<0, false>), g, b, 0, stream, c);
-  else hipLaunchKernelGGL((gemm_grouped_fp8_kernel<1, false>), g, b, 0, stream, c);
+  if (fp4) {
+    if (mode == 0) hipLaunchKernelGGL((gemm_grouped_fp8_kernel<0, true>), g, b, 0, stream, c);
+    else hipLaunchKernelGGL((gemm_grouped_fp8_kernel<1, true>), g, b, 0, stream, c);
+  } else {
+    if (mode == 0) hipLaunchKernelGGL((gemm_grouped_fp8_kernel<0, false>), g, b, 0, stream, c);
+    else hipLaunchKernelGGL((gemm_grouped_fp8_kernel<1, false>), g, b, 0, stream, c);
+  }
   return hipGetLastError();
 }
 

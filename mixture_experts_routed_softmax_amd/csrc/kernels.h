@@ -123,12 +123,14 @@ hipError_t launch_gemm_packed(const GemmArgs& a, int wfmt, int mode, int grid, h
 // 4 GiB (32-bit row offsets); gemm_packed_kernel serves the rest.
 bool gemm_grouped_bf16_fits(int64_t act_rows, int K);
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream);
-// fp8 (e4m3, 128 x 128 block scales) grouped GEMM on packed weights with one
-// wave per SIMD, 128 token rows per tile; takes K a multiple of 128 up to
+// fp8 (e4m3, 128 x 128 block scales) or, with fp4, e2m1 (UE8M0 scales per
+// 32 K) grouped GEMM on packed weights and e4m3 activations with one wave per
+// SIMD, 128 token rows per tile; takes K a multiple of 128 up to
 // 128 * kStreamMaxScaleBlocks and activations spanning at most 4 GiB.
 // Mode 0 gate/up (fp8 h and its scales), mode 1 down (bf16 y only).
 bool gemm_grouped_fp8_fits(int64_t act_rows, int K);
-hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode, int grid, hipStream_t stream);
+hipError_t launch_gemm_grouped_fp8(const GemmArgs& a, int64_t act_rows, int mode, bool fp4, int grid,
+                                   hipStream_t stream);
 constexpr int kPackedGateUpChannels = 128;   // h channels per packed gate/up tile (256 weight rows)
 constexpr int kPackedDownChannels = 256;     // output channels per packed down tile
 // weight-streaming GEMM for T <= 64 on packed weights (one 64-row tile per

@@ -28,6 +28,11 @@ SMALL = {
     "fp4": synthetic.spec("dsv3_fp4", T=100, H=256, I=384, E=16, k=4),
     # a long reduction (64 K steps of the grouped kernel's pipeline)
     "bf16_long_k": synthetic.spec("dsv3_bf16", T=96, H=4096, I=512, E=8, k=2),
+    # fp8 / fp4 grouped kernels past their three-block head (17 blocks of 128
+    # K), experts with several 32-row token tiles, and a down tile cut at
+    # H = 2176 (8.5 tiles of 256 channels)
+    "fp8_long_k": synthetic.spec("dsv3_fp8", T=160, H=2176, I=640, E=4, k=2),
+    "fp4_long_k": synthetic.spec("dsv3_fp4", T=160, H=2176, I=640, E=4, k=2),
 }
 
 
