@@ -2,10 +2,10 @@
  * moe.h -- C ABI of libmoe, a routed mixture-of-experts forward for AMD
  * Instinct MI355X (gfx950).
  *
- * The operation ("Experts backends" page, opening paragraph): for every token
- * a router selects k of E experts; the token's hidden state is projected
- * through each selected expert's parameters and the k results are summed with
- * the routing weights.  Each expert is a gated MLP (backend table, row
+ * The operation ("Experts backends" page, opening paragraph): each token's
+ * router scores pick k of the E experts, every picked expert transforms the
+ * token's hidden state with its own weights, and the token's output is the
+ * sum of those k results, each scaled by its routing weight.  Each expert is a gated MLP (backend table, row
  * deepgemm_megamoe; section "SonicMoE"): a gate and an up projection combined
  * as act(gate) * up, with act = silu (SwiGLU, the default), gelu (GeGLU) or
  * relu (ReGLU) as desc->gate_act selects, then a down projection.  Tokens are first ordered by their

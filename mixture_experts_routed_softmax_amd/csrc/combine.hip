@@ -1,5 +1,6 @@
 // Weighted combine back to token order ("Experts backends", opening
-// paragraph: the expert outputs are aggregated with the routing weights):
+// paragraph: a token's output adds up its experts' results, each scaled by
+// its routing weight):
 //   out[t, :] = sum_{i<k} w[t, i] * y_sorted[inv[t*k + i], :]
 // fp32 sums in slot order, one rounding to the output type, no atomics.
 // One workgroup per (token, 2048 channels), 8 channels (one 16-byte bf16

@@ -8,9 +8,9 @@
  * computes every step in fp64, one token and one selected expert at a time.
  *
  * What is computed (page "Experts backends"):
- *   - opening paragraph: for each token a router selects k experts, the hidden
- *     state is projected through the selected experts' parameters and the
- *     results are aggregated with the routing weights;
+ *   - opening paragraph: each token's router scores pick k experts, each
+ *     picked expert transforms the token's hidden state with its own weights,
+ *     and the k results are added up, each scaled by its routing weight;
  *   - backend table, rows grouped_mm / deepgemm: tokens are ordered by their
  *     selected expert before one grouped GEMM;
  *   - backend table, row deepgemm_megamoe, and section "SonicMoE": each expert is
