@@ -1,4 +1,7 @@
-// Grouped GEMMs of the expert MLPs on tile-packed weights (bf16 or OCP fp8).
+// Grouped GEMMs of the expert MLPs on tile-packed weights (bf16, OCP fp8 or
+// fp4).  The one-wave-per-SIMD grouped kernels (gemm_grouped.hip,
+// gemm_grouped_fp8.hip) take every shape they can address; this kernel runs
+// the rest: activations past 4 GiB and down projections with an f32 y.
 //
 // "Experts backends": each expert is a gated MLP (backend table, row
 // deepgemm_megamoe: up projection, SwiGLU, down projection) and all experts

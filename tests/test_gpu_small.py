@@ -131,10 +131,11 @@ def test_forward_f32_intermediate_rows(layout):
     _check_forward(s, L, hl, y_dtype="f32", layout=layout)
 
 
-def test_fp8_forward_f32_intermediate_rows():
-    """fp8 experts with float32 y rows: the down projection then runs on the
-    packed fp8 kernel (the grouped fp8 kernel writes bf16 y only)."""
-    s = SMALL["fp8_f32"]
+@pytest.mark.parametrize("name", ["fp8_f32", "fp4_long_k"])
+def test_fp8_forward_f32_intermediate_rows(name):
+    """fp8 / fp4 experts with float32 y rows: the down projection then runs on
+    the packed kernel (the grouped e4m3 kernel writes bf16 y only)."""
+    s = SMALL[name]
     L, hl = _layer(s, seed=4)
     _check_forward(s, L, hl, y_dtype="f32", layout="packed")
 
