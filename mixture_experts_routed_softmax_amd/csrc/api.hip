@@ -219,6 +219,7 @@ int grid_for(int64_t cap, int chunk = kXcdChunk) {
 struct PermuteWs {
   int32_t* block_counts;
   int32_t* block_base;
+  int32_t* sched_tables;   // scan -> scatter: what the schedules' items are computed from
   uint8_t* xq;
   float* xs;
 };
@@ -228,6 +229,7 @@ PermuteWs carve_permute(Carve& c, const moe_desc* d, bool with_quant) {
   PermuteWs w{};
   w.block_counts = c.take<int32_t>((size_t)nb * d->E);
   w.block_base = c.take<int32_t>((size_t)nb * d->E);
+  w.sched_tables = c.take<int32_t>(kSchedTablesInts);
   if (with_quant) {
     w.xq = c.take<uint8_t>((size_t)d->T * d->H);
     w.xs = c.take<float>((size_t)d->T * (d->H / 128));
@@ -404,12 +406,14 @@ moe_status run_permute(const moe_desc* d, const int32_t* ids, int32_t* counts, i
   }
   {
     StageTimer tm(MOE_STAGE_SCAN, st);
-    MOE_TRY_HIP(launch_scan(pw.block_counts, nb, d->E, counts, offsets, pw.block_base, touched, s0, s1, st),
+    MOE_TRY_HIP(launch_scan(pw.block_counts, nb, d->E, counts, offsets, pw.block_base, touched, s0, s1,
+                            pw.sched_tables, st),
                 "scan launch");
   }
   {
     StageTimer tm(MOE_STAGE_SCATTER, st);
-    MOE_TRY_HIP(launch_scatter(ids, P, d->E, pw.block_base, perm, inv, st), "scatter launch");
+    MOE_TRY_HIP(launch_scatter(ids, P, d->E, pw.block_base, perm, inv, s0, s1, pw.sched_tables, st),
+                "scatter launch");
   }
   return MOE_OK;
 }

@@ -42,12 +42,16 @@ constexpr int kGroupedXcdChunk = 16;
 
 hipError_t launch_hist(const int32_t* ids, int64_t P, int E, int32_t* block_counts,
                        hipStream_t stream);
-// counts, offsets, block bases, touched-expert list and up to two schedules.
+// counts, offsets, block bases, touched-expert list and the item counts of
+// up to two schedules; the tables their items are computed from go to
+// `tables` (kSchedTablesInts ints), and launch_scatter writes the items.
+constexpr int kSchedTablesInts = 5 * (kMaxExperts + 1) + 3;
 hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int32_t* counts,
                        int32_t* offsets, int32_t* block_base, int32_t* touched,
-                       SchedRequest s0, SchedRequest s1, hipStream_t stream);
+                       SchedRequest s0, SchedRequest s1, int32_t* tables, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* block_base,
-                          int32_t* perm, int32_t* inv, hipStream_t stream);
+                          int32_t* perm, int32_t* inv, SchedRequest s0, SchedRequest s1,
+                          const int32_t* tables, hipStream_t stream);
 // top-k selection of every token from the partial logits of
 // launch_route_logits, then hist + scan + scatter, in one workgroup, for
 // T <= kSelectPermuteMaxT and T * k <= kPermChunk

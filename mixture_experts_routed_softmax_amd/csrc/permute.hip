@@ -172,16 +172,27 @@ struct CountsOfOffsets {  // differences of global offsets
   __device__ int operator()(int e) const { return o[e + 1] - o[e]; }
 };
 
+// Layout of the schedule tables one launch hands to another (ints): row
+// offsets (E + 1), row tiles and first items of schedule 0, then of schedule
+// 1 (E each, at strides of kMaxExperts + 1), then the two item counts and
+// the row count.
+constexpr int kTabOff = 0, kTabTiles0 = kMaxExperts + 1, kTabBase0 = 2 * (kMaxExperts + 1),
+              kTabTiles1 = 3 * (kMaxExperts + 1), kTabBase1 = 4 * (kMaxExperts + 1),
+              kTabTotals = 5 * (kMaxExperts + 1);
+static_assert(kTabTotals + 3 == kSchedTablesInts, "schedule table layout");
+
 // From the expert counts count_of(e), e < E (written, if in LDS, before a
 // barrier): the counts in counts_out (if not null), the exclusive offsets in
 // s_offsets[0..E) and their total (the row count, also stored at s_offsets[E]
 // by thread 0: read it there only after a barrier), the touched-expert list
 // (ascending, its length in touched[E]; touched may be null) and up to two
 // grouped-GEMM schedules (a null sched skips one), with a single four-way scan.
+// With `tables` the schedules' items are left to another launch: their item
+// counts go to the headers and the tables they are computed from to `tables`.
 template <class CountOf>
 __device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__ counts_out, int* s_offsets, int E,
                                          int32_t* __restrict__ touched, SchedRequest s0, SchedRequest s1,
-                                         int* s_work, int* s_tmp) {
+                                         int* s_work, int* s_tmp, int32_t* __restrict__ tables = nullptr) {
   const int tid = threadIdx.x;
   int* s_tiles0 = s_work;
   int* s_tiles1 = s_work + (kMaxExperts + 1);
@@ -215,6 +226,22 @@ __device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__
     if (s0.sched != nullptr) s0.sched->total = total[1];
     if (s1.sched != nullptr) s1.sched->total = total[2];
   }
+  if (tables != nullptr) {
+    for (int e = tid; e < E; e += 1024) {
+      tables[kTabOff + e] = s_offsets[e];
+      tables[kTabTiles0 + e] = s_tiles0[e];
+      tables[kTabBase0 + e] = s_base0[e];
+      tables[kTabTiles1 + e] = s_tiles1[e];
+      tables[kTabBase1 + e] = s_base1[e];
+    }
+    if (tid == 0) {
+      tables[kTabOff + E] = total[0];
+      tables[kTabTotals] = total[1];
+      tables[kTabTotals + 1] = total[2];
+      tables[kTabTotals + 2] = total[0];
+    }
+    return total[0];
+  }
   // both schedules' items in one pass (totals of a null schedule are 0)
   for (int idx = tid; idx < total[1] + total[2]; idx += 1024) {
     const bool first = idx < total[1];
@@ -227,7 +254,7 @@ __device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__
 __global__ __launch_bounds__(1024) void scan_kernel(
     const int32_t* __restrict__ block_counts, int64_t nblocks, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ block_base, int32_t* __restrict__ touched,
-    SchedRequest s0, SchedRequest s1) {
+    SchedRequest s0, SchedRequest s1, int32_t* __restrict__ tables) {
   __shared__ int s_part[4][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
@@ -257,7 +284,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   }
   __syncthreads();
   const int total =
-      scan_counts_and_schedules(CountsInLds{s_offsets}, nullptr, s_offsets, E, touched, s0, s1, s_work, s_tmp);
+      scan_counts_and_schedules(CountsInLds{s_offsets}, nullptr, s_offsets, E, touched, s0, s1, s_work, s_tmp, tables);
   for (int i = tid; i <= E; i += 1024) offsets[i] = i < E ? s_offsets[i] : total;
   // per-chunk bases
   if (e < E) {
@@ -357,19 +384,30 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
 // One workgroup of 1024 threads per chunk of 1024 pairs (one pair each): the
 // rank among the wave's earlier lanes with the same id, the wave's count of
 // each id (written by its last lane with that id), then the row: the
-// chunk's base for the expert + the earlier waves' counts + the rank.
+// chunk's base for the expert + the earlier waves' counts + the rank.  The
+// workgroups also write the schedules' items from the tables scan_kernel
+// left (item idx by thread idx of the grid): spread over the grid, the
+// per-item arithmetic costs a fraction of what it costs one workgroup.
 __global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
                                                        int E, const int32_t* __restrict__ block_base,
                                                        int32_t* __restrict__ perm,
-                                                       int32_t* __restrict__ inv) {
+                                                       int32_t* __restrict__ inv, SchedRequest s0,
+                                                       SchedRequest s1, const int32_t* __restrict__ tables) {
   static_assert(kPermChunk == 1024, "one pair per thread");
   __shared__ int s_cursor[kMaxExperts];
   __shared__ int s_wcount[16][kMaxExperts];
+  __shared__ int s_tab[kSchedTablesInts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t p = (int64_t)blockIdx.x * kPermChunk + tid;
   int e = p < P ? ids[p] : -1;
   for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&s_wcount[0][0])[x] = 0;
   for (int x = tid; x < E; x += 1024) s_cursor[x] = block_base[(int64_t)blockIdx.x * E + x];
+  for (int x = tid; x < 5 * (E + 1); x += 1024) {
+    const int t = x / (E + 1), i = x - t * (E + 1);   // table t, entry i <= E
+    const int o = t * (kMaxExperts + 1) + i;
+    if (t == 0 || i < E) s_tab[o] = tables[o];
+  }
+  if (tid < 3) s_tab[kTabTotals + tid] = tables[kTabTotals + tid];
   __syncthreads();
   if ((unsigned)e >= (unsigned)E) e = -1;   // out-of-range ids get no row
   int n_same;
@@ -383,6 +421,12 @@ __global__ __launch_bounds__(1024) void scatter_kernel(const int32_t* __restrict
     inv[p] = row;
   } else if (p < P) {
     inv[p] = -1;   // a pair with an out-of-range id has no row
+  }
+  const int n0 = s_tab[kTabTotals], n1 = s_tab[kTabTotals + 1], rows_total = s_tab[kTabTotals + 2];
+  for (int idx = blockIdx.x * 1024 + tid; idx < n0 + n1; idx += gridDim.x * 1024) {
+    const bool first = idx < n0;
+    write_schedule_item(s_tab + kTabOff, E, rows_total, first ? s0 : s1, s_tab + (first ? kTabTiles0 : kTabTiles1),
+                        s_tab + (first ? kTabBase0 : kTabBase1), first ? idx : idx - n0);
   }
 }
 
@@ -442,18 +486,21 @@ hipError_t launch_hist(const int32_t* ids, int64_t P, int E, int32_t* block_coun
 
 hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int32_t* counts,
                        int32_t* offsets, int32_t* block_base, int32_t* touched, SchedRequest s0,
-                       SchedRequest s1, hipStream_t stream) {
+                       SchedRequest s1, int32_t* tables, hipStream_t stream) {
+  if (tables == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, block_counts, nblocks, E, counts,
-                     offsets, block_base, touched, s0, s1);
+                     offsets, block_base, touched, s0, s1, tables);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const int32_t* ids, int64_t P, int E, const int32_t* block_base,
-                          int32_t* perm, int32_t* inv, hipStream_t stream) {
+                          int32_t* perm, int32_t* inv, SchedRequest s0, SchedRequest s1,
+                          const int32_t* tables, hipStream_t stream) {
   int64_t nb = perm_blocks(P);
   if (nb == 0) return hipSuccess;
+  if (tables == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, ids, P, E,
-                     block_base, perm, inv);
+                     block_base, perm, inv, s0, s1, tables);
   return hipGetLastError();
 }
 
