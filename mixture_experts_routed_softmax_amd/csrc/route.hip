@@ -129,16 +129,18 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
 }
 
 // ------------------------------------------------- LDS-staged router (large T)
-// For large batches: a workgroup owns 64 tokens and all experts (padded to
-// kEP = 64, 128 or 256 rows) over a K slice.  The token and router rows of a
+// For large batches: a workgroup owns 64 tokens (128 for kEP = 256) and all
+// experts (padded to kEP = 64, 128 or 256 rows) over a K slice.  The token and router rows of a
 // 64-deep K chunk are brought into LDS by global_load_lds (one 1 KB
 // instruction = 8 rows x 128 B, rows swizzled chunk ^ (row & 7)), 3 chunks in
 // flight, so each row is read once per workgroup in whole cache lines.
 // 8 waves; kWT = 8 / (kEP / 32) waves share a 32-expert tile: one wave takes
-// both token tiles, two waves one token tile each, four waves one token tile
+// every token tile, two waves one token tile each, four waves one token tile
 // and every other 16-deep slice (their partial tiles are added in a fixed
 // order).  The slice's logits go to part[slice][t][e] as in logits_kernel.
-constexpr int kBigTok = 64;
+// tokens per workgroup: 128 when the experts pad to 256 rows (the router
+// rows, re-read by every workgroup, then carry twice the tokens), else 64
+__host__ __device__ constexpr int big_tok(int ep) { return ep > 128 ? 128 : 64; }
 constexpr int kRouteStages = 3;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -153,13 +155,16 @@ template <int kEP>
 __global__ __launch_bounds__(512) void logits_lds_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wr, int64_t T, int H,
                                                          int E, int chunks_per_slice, float* __restrict__ part) {
+  constexpr int kBigTok = big_tok(kEP);
   constexpr int kXB = kBigTok * 128;                  // token bytes per stage
   constexpr int kStage = kXB + kEP * 128;
+  constexpr int kXI = kBigTok / 64;                   // token DMA instructions per wave per chunk
   constexpr int kWI = kEP / 64;                       // router DMA instructions per wave per chunk
-  constexpr int kLoads = 1 + kWI;
+  constexpr int kLoads = kXI + kWI;
   constexpr int kET = kEP / 32, kWT = 8 / kET;       // expert tiles, waves per expert tile
-  constexpr int kNJ = kWT == 1 ? 2 : 1;               // token tiles per wave
+  constexpr int kNJ = kWT == 1 ? kBigTok / 32 : 1;    // token tiles per wave
   constexpr int kUStep = kWT == 4 ? 2 : 1;            // 16-deep slices: every kUStep-th
+  static_assert(kWT == 1 || kBigTok == 64, "two or four waves per expert tile split 64 tokens");
   static_assert((kEP + 1) * kBigTok * 4 <= kRouteStages * kStage, "logit tile fits the ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRouteStages * kStage];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -169,14 +174,15 @@ __global__ __launch_bounds__(512) void logits_lds_kernel(const uint16_t* __restr
   const int nchunks = H / 64;
   const int c0 = blockIdx.y * chunks_per_slice;
   const int c1 = min(nchunks, c0 + chunks_per_slice);
-  // DMA sources: token row wave*8 + lane/8, router rows (i*8 + wave)*8 + lane/8
+  // DMA sources: token rows (i*8 + wave)*8 + lane/8, router rows likewise
   const int slot = lane & 7;
-  const uint16_t* xsrc;
-  {
-    const int r = wv * 8 + (lane >> 3);
+  const uint16_t* xsrc[kXI];
+#pragma unroll
+  for (int i = 0; i < kXI; ++i) {
+    const int r = (i * 8 + wv) * 8 + (lane >> 3);
     int64_t t = t0 + r;
     t = t < T ? t : T - 1;
-    xsrc = x + t * H + ((slot ^ (r & 7)) * 8);
+    xsrc[i] = x + t * H + ((slot ^ (r & 7)) * 8);
   }
   const uint16_t* wsrc[kWI];
 #pragma unroll
@@ -187,7 +193,8 @@ __global__ __launch_bounds__(512) void logits_lds_kernel(const uint16_t* __restr
   }
   auto issue = [&](int stage, int c) {
     uint8_t* sb = smem + stage * kStage;
-    route_lds_load16(xsrc + c * 64, sb + wv * 1024);
+#pragma unroll
+    for (int i = 0; i < kXI; ++i) route_lds_load16(xsrc[i] + c * 64, sb + (i * 8 + wv) * 1024);
 #pragma unroll
     for (int i = 0; i < kWI; ++i) route_lds_load16(wsrc[i] + c * 64, sb + kXB + (i * 8 + wv) * 1024);
   };
@@ -259,7 +266,8 @@ bool route_big(int64_t T, int H) { return T >= 256 && H % 64 == 0; }
 
 int route_slices(int64_t T, int H, int E) {
   if (route_big(T, H)) {
-    const int64_t tiles = (T + kBigTok - 1) / kBigTok;
+    const int tok = big_tok(E > 128 ? 256 : (E > 64 ? 128 : 64));
+    const int64_t tiles = (T + tok - 1) / tok;
     const int nchunks = H / 64;
     int64_t sl = (256 + tiles - 1) / tiles;
     const int max_sl = nchunks / 4 > 0 ? nchunks / 4 : 1;   // at least 4 chunks per slice
@@ -301,11 +309,13 @@ hipError_t launch_route_topk(const void* x, const void* w_router, const float* b
     const int slices = route_slices(T, H, E);
     const int nchunks = H / 64;
     const int per = (nchunks + slices - 1) / slices;
-    dim3 grid((unsigned)((T + kBigTok - 1) / kBigTok), (unsigned)slices);
+    const int ep = E > 128 ? 256 : (E > 64 ? 128 : 64);
+    const int tok = big_tok(ep);
+    dim3 grid((unsigned)((T + tok - 1) / tok), (unsigned)slices);
     const uint16_t* xb = (const uint16_t*)x;
     const uint16_t* wb = (const uint16_t*)w_router;
-    if (E <= 64) hipLaunchKernelGGL(logits_lds_kernel<64>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
-    else if (E <= 128) hipLaunchKernelGGL(logits_lds_kernel<128>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
+    if (ep == 64) hipLaunchKernelGGL(logits_lds_kernel<64>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
+    else if (ep == 128) hipLaunchKernelGGL(logits_lds_kernel<128>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
     else hipLaunchKernelGGL(logits_lds_kernel<256>, grid, dim3(512), 0, stream, xb, wb, T, H, E, per, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

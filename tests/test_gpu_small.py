@@ -23,6 +23,9 @@ SMALL = {
     "bf16_sigmoid": synthetic.spec("dsv3_bf16", T=130, H=256, I=256, E=16),
     # >= 256 tokens take the LDS-staged router; 100 experts pad to 128 rows
     "bf16_e100": synthetic.spec("dsv3_bf16", T=320, H=384, I=256, E=100, k=6),
+    # 160 experts pad to 256 rows: 128-token router workgroups (the last one
+    # ragged) over 4 K slices
+    "bf16_e160": synthetic.spec("dsv3_bf16", T=300, H=1024, I=256, E=160, k=6),
     "fp8_f32": synthetic.spec("dsv3_fp8", T=100, H=256, I=384, E=16, k=4),
     "fp8_ue8m0": synthetic.spec("dsv3_fp8", T=100, H=256, I=384, E=16, k=4, scale_fmt="ue8m0"),
     "fp4": synthetic.spec("dsv3_fp4", T=100, H=256, I=384, E=16, k=4),
