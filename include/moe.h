@@ -337,8 +337,11 @@ const char* moe_last_error(void);
  * number of timed launches into launches[stage] (both host arrays of
  * MOE_NUM_STAGES entries), and clears the record.  Not thread-safe.
  * When all T*k pairs fit one 1024-pair chunk, histogram, scan and scatter run
- * as one launch, timed under MOE_STAGE_SCAN.  A stage's time covers all of its
- * launches (the weight-streaming GEMMs add a split-K reduction launch). */
+ * as one launch, timed under MOE_STAGE_SCAN; up to 32 chunks the histogram
+ * runs inside the scan launch (MOE_STAGE_SCAN), and MOE_STAGE_HIST times a
+ * histogram launch only past that.  A stage's time covers all of its
+ * launches (the weight-streaming gate/up and down add a split-K reduction
+ * launch each). */
 enum {
     MOE_STAGE_ROUTE = 0, MOE_STAGE_HIST = 1, MOE_STAGE_SCAN = 2, MOE_STAGE_SCATTER = 3,
     MOE_STAGE_QUANT_X = 4, MOE_STAGE_GATE_UP = 5, MOE_STAGE_DOWN = 6, MOE_STAGE_COMBINE = 7,

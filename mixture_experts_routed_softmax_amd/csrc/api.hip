@@ -400,11 +400,15 @@ moe_status run_permute(const moe_desc* d, const int32_t* ids, int32_t* counts, i
                 "permute launch");
     return MOE_OK;
   }
-  {
-    StageTimer tm(MOE_STAGE_HIST, st);
-    MOE_TRY_HIP(launch_hist(ids, P, d->E, pw.block_counts, st), "histogram launch");
-  }
-  {
+  if (nb <= kFusedHistBlocks) {
+    StageTimer tm(MOE_STAGE_SCAN, st);
+    MOE_TRY_HIP(launch_hist_scan(ids, P, d->E, counts, offsets, pw.block_base, touched, s0, s1, pw.sched_tables, st),
+                "histogram and scan launch");
+  } else {
+    {
+      StageTimer tm(MOE_STAGE_HIST, st);
+      MOE_TRY_HIP(launch_hist(ids, P, d->E, pw.block_counts, st), "histogram launch");
+    }
     StageTimer tm(MOE_STAGE_SCAN, st);
     MOE_TRY_HIP(launch_scan(pw.block_counts, nb, d->E, counts, offsets, pw.block_base, touched, s0, s1,
                             pw.sched_tables, st),

@@ -251,15 +251,41 @@ __device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__
   return total[0];
 }
 
+// kFusedHist: the histogram of every chunk is taken here too, from the ids
+// (at most kFusedHistBlocks chunks, chunk c by wave c % 16 with LDS atomics
+// into its own row of counts), so that no histogram launch precedes the scan.
+template <bool kFusedHist>
 __global__ __launch_bounds__(1024) void scan_kernel(
-    const int32_t* __restrict__ block_counts, int64_t nblocks, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ block_base, int32_t* __restrict__ touched,
-    SchedRequest s0, SchedRequest s1, int32_t* __restrict__ tables) {
+    const int32_t* __restrict__ ids, int64_t P, const int32_t* __restrict__ block_counts, int64_t nblocks, int E,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ block_base,
+    int32_t* __restrict__ touched, SchedRequest s0, SchedRequest s1, int32_t* __restrict__ tables) {
   __shared__ int s_part[4][kMaxExperts];
   __shared__ int s_offsets[kMaxExperts + 1];
   __shared__ int s_work[kSchedWork];
   __shared__ int s_tmp[4];   // the scans' totals
+  __shared__ int s_cnt[kFusedHist ? kFusedHistBlocks * kMaxExperts : 1];
   const int tid = threadIdx.x;
+  if constexpr (kFusedHist) {
+    for (int x = tid; x < (int)nblocks * E; x += 1024) s_cnt[x] = 0;
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int c = wave; c < (int)nblocks; c += 16) {
+      int v[kPermChunk / 64];
+#pragma unroll
+      for (int q = 0; q < kPermChunk / 64; ++q) {
+        const int64_t p = (int64_t)c * kPermChunk + q * 64 + lane;
+        v[q] = p < P ? ids[p] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < kPermChunk / 64; ++q)
+        if ((unsigned)v[q] < (unsigned)E) atomicAdd(&s_cnt[c * E + v[q]], 1);   // out-of-range ids are ignored
+    }
+    __syncthreads();
+  }
+  auto chunk_count = [&](int64_t b, int ex) {
+    if constexpr (kFusedHist) return s_cnt[b * E + ex];
+    else return block_counts[b * E + ex];
+  };
   const int e = tid & 255;
   const int part = tid >> 8;
   const int64_t per = (nblocks + 3) / 4;
@@ -271,7 +297,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     for (int64_t b = b0; b < b1; b += 8) {
       int c[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? block_counts[(b + u) * E + e] : 0;
+      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? chunk_count(b + u, e) : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) sum += c[u];
     }
@@ -293,7 +319,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     for (int64_t b = b0; b < b1; b += 8) {
       int c[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? block_counts[(b + u) * E + e] : 0;
+      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? chunk_count(b + u, e) : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (b + u < b1) {
@@ -488,8 +514,18 @@ hipError_t launch_scan(const int32_t* block_counts, int64_t nblocks, int E, int3
                        int32_t* offsets, int32_t* block_base, int32_t* touched, SchedRequest s0,
                        SchedRequest s1, int32_t* tables, hipStream_t stream) {
   if (tables == nullptr) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, block_counts, nblocks, E, counts,
-                     offsets, block_base, touched, s0, s1, tables);
+  hipLaunchKernelGGL(scan_kernel<false>, dim3(1), dim3(1024), 0, stream, nullptr, (int64_t)0, block_counts, nblocks,
+                     E, counts, offsets, block_base, touched, s0, s1, tables);
+  return hipGetLastError();
+}
+
+hipError_t launch_hist_scan(const int32_t* ids, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                            int32_t* block_base, int32_t* touched, SchedRequest s0, SchedRequest s1,
+                            int32_t* tables, hipStream_t stream) {
+  const int64_t nb = perm_blocks(P);
+  if (tables == nullptr || nb > kFusedHistBlocks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_kernel<true>, dim3(1), dim3(1024), 0, stream, ids, P, nullptr, nb, E, counts, offsets,
+                     block_base, touched, s0, s1, tables);
   return hipGetLastError();
 }
 

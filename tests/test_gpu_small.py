@@ -450,7 +450,7 @@ def test_stage_timing_counts_every_launch():
     """Stage timing: every launch of a forward is counted once under its
     stage with a positive duration (launches of one call are timed back to
     back), and the stage times of a call add up to no more than its wall time."""
-    s = SMALL["bf16_softmax"]            # 1200 pairs: the three-launch permutation
+    s = SMALL["bf16_softmax"]            # 1200 pairs: the multi-chunk permutation (histogram inside the scan)
     L, _ = _layer(s)
     run_forward(s, L, layout="packed")
     torch.cuda.synchronize()
@@ -464,9 +464,10 @@ def test_stage_timing_counts_every_launch():
     torch.cuda.synchronize()
     st = moe.moe_timing_read()
     moe.moe_timing_enable(False)
-    for name in ("route", "hist", "scan", "scatter", "gate_up", "down", "combine"):
+    for name in ("route", "scan", "scatter", "gate_up", "down", "combine"):
         ms, n = st[name]
         assert n == 3 and ms > 0, (name, ms, n)
+    assert st["hist"][1] == 0   # at most 32 chunks: no histogram launch of its own
     assert sum(ms for ms, _ in st.values()) <= start.elapsed_time(stop) * 1.001
     assert moe.moe_timing_read()["gate_up"][1] == 0
 
@@ -507,6 +508,32 @@ def test_nan_token(name, T, layout):
     ref = oracle_experts(s, hl).combine(hl["x"], ids_o, w_o, rest)
     assert np.isfinite(o[rest]).all()
     assert row_rel_err(o[rest], ref) <= tol_of(s)
+
+
+@pytest.mark.parametrize("T", [2049, 4096, 4097, 8193])
+def test_permute_histogram_paths(T):
+    """Up to 32 chunks of 1024 pairs the chunk histograms are taken inside the
+    scan launch (T = 2049 and 4096 with k = 8: 17 and 32 chunks); above that
+    a histogram launch precedes it (T = 4097 and 8193: 33 and 65 chunks).
+    Skewed ids, checked bit for bit against the oracle's permutation."""
+    s = synthetic.spec("dsv3_bf16", T=T, H=128, I=128, E=256, k=8)
+    rng = np.random.default_rng(T)
+    pz = 1.0 / np.arange(1, s.E + 1) ** 1.1
+    ids = rng.choice(s.E, size=(T, s.k), p=pz / pz.sum()).astype(np.int32)
+    counts_o, offsets_o, perm_o, inv_o = oracle.permute(ids, s.E)
+    d = desc_for(s)
+    P = T * s.k
+    counts = torch.empty(s.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(P, dtype=torch.int32, device="cuda")
+    inv = torch.empty(P, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d, torch.from_numpy(ids).cuda(), None, counts, offsets, perm, inv,
+                    ws=moe.workspace(d, moe.MOE_OP_PERMUTE))
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), counts_o)
+    assert np.array_equal(offsets.cpu().numpy(), offsets_o)
+    assert np.array_equal(perm.cpu().numpy(), perm_o)
+    assert np.array_equal(inv.cpu().numpy(), inv_o)
 
 
 @pytest.mark.parametrize("T", [100, 1500])
