@@ -487,6 +487,13 @@ def main():
                 "kernel": "gate_up grouped GEMM (%s)" % s.experts,
                 "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": flops,
                 "layer_tflops": round(layer_tflops, 1), "layer_frac": round(layer_tflops / peak, 4)}
+        # the layer against the HBM roofline as well: the touched experts'
+        # weights read once, x read and out written once (bf16), over the step
+        act_b = 2 if s.act == "bf16" else 4
+        layer_bytes = touched * weight_bytes_per_expert(s) + 2 * s.T * s.H * act_b
+        layer_gbs = layer_bytes / (ms_per_step / 1e3) / 1e9
+        roof["layer_hbm"] = {"alg_bytes": layer_bytes, "achieved_GBs": round(layer_gbs, 1),
+                             "peak_GBs": PEAK_HBM_GBS, "frac": round(layer_gbs / PEAK_HBM_GBS, 4)}
     log("layer: %.3f ms/step, %.0f tokens/s, %.1f TFLOP/s expert GEMMs, touched %d/%d experts, "
         "max/mean tokens per expert %d/%.1f"
         % (ms_per_step, value, layer_tflops, touched, s.E, int(cnt.max()), P / s.E))
