@@ -477,26 +477,36 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restr
 }
 
 // Dynamic fp8 quantization of bf16 rows, per 128 channels: s = amax/448,
-// code = RNE_e4m3(x/s); amax = 0 gives s = 1 and zero codes.
+// code = RNE_e4m3(x/s); amax = 0 gives s = 1 and zero codes.  A thread takes
+// 8 channels (one 16-byte load), 16 threads a group, a workgroup 16 groups
+// (2048 channels) of one row.  (One 4-byte load per lane and a wave per group
+// ran at 2.5 TB/s: 71 us for the DeepSeek-like 8192 x 7168 rows.)
 __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __restrict__ x,
                                                              int n, uint8_t* __restrict__ codes,
                                                              float* __restrict__ scales) {
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int groups = n / 128;
-  {
-    const int g = blockIdx.y * 4 + wave;   // one 128-channel group per wave
-    if (g >= groups) return;
-    const uint32_t two = *(const uint32_t*)(x + row * n + g * 128 + 2 * lane);
-    float a = bf16_bits_to_f32((uint16_t)(two & 0xffff));
-    float b = bf16_bits_to_f32((uint16_t)(two >> 16));
-    float m = fmaxf(fabsf(a), fabsf(b));
+  const int c8 = blockIdx.y * 256 + threadIdx.x;   // 8-channel piece of the row
+  const int g = c8 >> 4;                           // its 128-channel group
+  const bool live = g < groups;                    // (uniform per 16 lanes)
+  i32x4 v = {0, 0, 0, 0};
+  if (live) v = *(const i32x4*)(x + row * n + c8 * 8);
+  float f[8];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float s = m > 0.f ? m / 448.0f : 1.0f;
-    uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(a / s, b / s, 0, false);
-    *(uint16_t*)(codes + row * n + g * 128 + 2 * lane) = (uint16_t)(pk & 0xffff);
-    if (lane == 0) scales[row * groups + g] = s;
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = bf16_bits_to_f32((uint16_t)((uint32_t)v[q] & 0xffff));
+    f[2 * q + 1] = bf16_bits_to_f32((uint16_t)((uint32_t)v[q] >> 16));
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float s = m > 0.f ? m / 448.0f : 1.0f;
+  if (live) {
+    *(i32x2*)(codes + row * n + c8 * 8) = i32x2{(int)pack_fp8x4(f[0] / s, f[1] / s, f[2] / s, f[3] / s),
+                                                (int)pack_fp8x4(f[4] / s, f[5] / s, f[6] / s, f[7] / s)};
+    if ((c8 & 15) == 0) scales[row * groups + g] = s;
   }
 }
 
@@ -585,7 +595,7 @@ hipError_t launch_gather_scales(const float* src, const int32_t* perm, int k, in
 hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int64_t rows, int n, uint8_t* codes,
                                  float* scales, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows, (unsigned)((n / 128 + 3) / 4)), dim3(256), 0,
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)rows, (unsigned)((n / 8 + 255) / 256)), dim3(256), 0,
                      stream, x_bf16, n, codes, scales);
   return hipGetLastError();
 }
