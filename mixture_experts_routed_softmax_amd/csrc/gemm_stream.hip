@@ -396,6 +396,18 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, const WorkItem& i
   stream_epilogue<kFp8, kMode, kOutF32, NT>(a, it, acc);
 }
 
+// Work item w: the schedule's entry, or with one entry per touched expert
+// (its whole segment: every expert holds at most 64 rows here) entry
+// w / wtiles with channel tile w % wtiles
+__device__ __forceinline__ WorkItem stream_item(const GemmArgs& a, int w) {
+  const WorkItem* items = (const WorkItem*)(a.sched + 1);
+  if (!a.per_expert_items) return items[w];
+  const int te = w / a.wtiles;
+  WorkItem it = items[te];
+  it.ntile = w - te * a.wtiles;
+  return it;
+}
+
 template <int kW, int kMode, bool kOutF32, bool kOneTile>
 __global__ __launch_bounds__(256, (kBlocksPerCu<kW, kOneTile>)) void gemm_stream_kernel(GemmArgs a) {
   const int items = a.sched->total;
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(256, (kBlocksPerCu<kW, kOneTile>)) void gemm_stream
   const int u = xcd_work_index(items * S);
   if (u < 0) return;
   const int w = u / S, sp = u - w * S;
-  const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
+  const WorkItem it = stream_item(a, w);
   // down without its reduction launch: where each sorted row's partial rows
   // are (the items of an expert's channel tiles are consecutive)
   if (kMode == 1 && a.rowinfo != nullptr && sp == 0 && it.ntile == 0 &&
@@ -431,7 +443,7 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(GemmArgs a) {
   const int S = stream_splits(items, KT, kSlots<kW, kOneTile>);
   const int w = blockIdx.x;
   if (S == 1 || w >= items) return;
-  const WorkItem it = ((const WorkItem*)(a.sched + 1))[w];
+  const WorkItem it = stream_item(a, w);
   const int rows = it.row_end - it.row_begin;
   const float* part = a.partial + (int64_t)w * S * kStreamPartFloats;
   const int tid = threadIdx.x, N = a.N;

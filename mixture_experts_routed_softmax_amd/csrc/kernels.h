@@ -34,6 +34,10 @@ struct SchedRequest {
   int capacity;       // items the buffer holds
   int block_m = 1;    // an expert's items run in blocks of block_m row tiles
   int block_n = 1;    //   x block_n channel tiles (see build_schedule)
+  // weight streaming (every expert's rows form one row tile): one entry per
+  // touched expert (its rows, channel tile 0) instead of one per item; item w
+  // is entry w / ntiles with channel tile w % ntiles (GemmArgs::per_expert_items)
+  bool implicit_items = false;
 };
 
 // work items per XCD chunk of the one-wave-per-SIMD grouped GEMMs
@@ -112,6 +116,7 @@ struct GemmArgs {
   int gu_out;               // row-major bf16 gate/up: store g and u (fp32 [P, 2N]) instead of h
   int64_t act_rows;         // rows of `act` (bounds of the activation buffer resource)
   int32_t* rowinfo;         // streaming down without its reduction launch: sorted row -> item * 64 + row in item
+  int per_expert_items;     // streaming: the schedule holds one entry per touched expert (see SchedRequest)
 };
 
 // tile geometry of the grouped GEMMs

@@ -226,6 +226,15 @@ __device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__
     if (s0.sched != nullptr) s0.sched->total = total[1];
     if (s1.sched != nullptr) s1.sched->total = total[2];
   }
+  // a streaming schedule gets one entry per touched expert (at its place in
+  // the touched list) and no per-item entries
+  for (int e = tid; e < E; e += 1024)
+    if (s_c[e] > 0) {
+      const WorkItem ent{s_offsets[e], s_offsets[e] + s_c[e], e, 0};
+      if (s0.implicit_items) ((WorkItem*)(s0.sched + 1))[s_tpos[e]] = ent;
+      if (s1.implicit_items) ((WorkItem*)(s1.sched + 1))[s_tpos[e]] = ent;
+    }
+  const int w0 = s0.implicit_items ? 0 : total[1], w1 = s1.implicit_items ? 0 : total[2];
   if (tables != nullptr) {
     for (int e = tid; e < E; e += 1024) {
       tables[kTabOff + e] = s_offsets[e];
@@ -236,17 +245,17 @@ __device__ int scan_counts_and_schedules(CountOf count_of, int32_t* __restrict__
     }
     if (tid == 0) {
       tables[kTabOff + E] = total[0];
-      tables[kTabTotals] = total[1];
-      tables[kTabTotals + 1] = total[2];
+      tables[kTabTotals] = w0;
+      tables[kTabTotals + 1] = w1;
       tables[kTabTotals + 2] = total[0];
     }
     return total[0];
   }
   // both schedules' items in one pass (totals of a null schedule are 0)
-  for (int idx = tid; idx < total[1] + total[2]; idx += 1024) {
-    const bool first = idx < total[1];
+  for (int idx = tid; idx < w0 + w1; idx += 1024) {
+    const bool first = idx < w0;
     write_schedule_item(s_offsets, E, total[0], first ? s0 : s1, first ? s_tiles0 : s_tiles1,
-                        first ? s_base0 : s_base1, first ? idx : idx - total[1]);
+                        first ? s_base0 : s_base1, first ? idx : idx - w0);
   }
   return total[0];
 }
