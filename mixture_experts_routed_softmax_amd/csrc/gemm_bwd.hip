@@ -510,22 +510,40 @@ __global__ __launch_bounds__(256) void bias_grad_kernel(const float* __restrict_
   if (threadIdx.x == 0) dbias[e] = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
 }
 
-// dx[t] = sum_i dxp[inv[t*k+i]] + dxr[t] (slot order, fp32), rounded to bf16
+// dx[t] = sum_i dxp[inv[t*k+i]] + dxr[t] (slot order, fp32), rounded to bf16.
+// The token's rows are read from inv once into LDS, then the loads of up to 8
+// slots are issued together (streaming: every row is read once): qwen-like
+// backward 48 -> 31 us
 __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dxp, const float* __restrict__ dxr,
                                                          const int32_t* __restrict__ inv, int k, int H,
                                                          uint16_t* __restrict__ dx) {
+  __shared__ int s_row[kMaxTopK];
   const int64_t t = blockIdx.x;
+  const int64_t P = (int64_t)gridDim.x * k;
+  if ((int)threadIdx.x < k) {
+    const int64_t row = inv[t * k + threadIdx.x];
+    s_row[threadIdx.x] = row >= 0 && row < P ? (int)row : -1;   // a pair without a row contributes nothing
+  }
+  __syncthreads();
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= H) return;
-  f32x4 acc = *(const f32x4*)(dxr + t * H + c);
+  f32x4 acc = __builtin_nontemporal_load((const f32x4*)(dxr + t * H + c));
   f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int64_t P = (int64_t)gridDim.x * k;
-  for (int i = 0; i < k; ++i) {
-    const int64_t row = inv[t * k + i];
-    if (row < 0 || row >= P) continue;   // a pair without a row contributes nothing
-    const f32x4 v = *(const f32x4*)(dxp + row * H + c);
+  for (int i0 = 0; i0 < k; i0 += 8) {
+    f32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] += v[q];
+    for (int u = 0; u < 8; ++u) {
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i0 + u < k && s_row[i0 + u] >= 0)
+        v[u] = __builtin_nontemporal_load((const f32x4*)(dxp + (int64_t)s_row[i0 + u] * H + c));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u >= k) break;
+      if (s_row[i0 + u] < 0) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum[q] += v[u][q];
+    }
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = sum[q] + acc[q];
